@@ -144,8 +144,12 @@ class Drawn:
     v: np.ndarray
     do: Optional[np.ndarray]
 
-    def f64(self, name: str) -> np.ndarray:
-        return bits_to_f64(getattr(self, name), self.dtype)
+    def f64(self, name: str, b: Optional[int] = None, h: Optional[int] = None) -> np.ndarray:
+        """float64 copy of a whole tensor, or of head (b, h) only."""
+        x = getattr(self, name)
+        if b is not None:
+            x = x[b, h]
+        return bits_to_f64(x, self.dtype)
 
 
 def draw(B: int, H: int, N: int, d: int, dtype: str, seed: int,

@@ -1,0 +1,130 @@
+// C ABI layer: argument validation (before any HIP call) and kernel dispatch.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+// A failed launch is reported once on stderr with HIP's own description, then
+// surfaces to the caller as FA_ERR_HIP.
+fa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return FA_OK;
+  fprintf(stderr, "libfa: %s: %s (%d)\n", where, hipGetErrorString(e), (int)e);
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  // element count must fit comfortably in signed 64-bit and grid dims in 31 bits
+  const long double elems = (long double)B * H * (long double)N * d;
+  if (elems > 9.0e18L) return FA_ERR_SHAPE;
+  // the dispatch grid counts work-items in 32 bits: blocks * 256 threads < 2^32
+  const long double blocks = (long double)B * H * ((N + 31) / 32 + 1);
+  if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa_status check_dtype(fa_dtype dt) { return (dt == FA_F16 || dt == FA_BF16) ? FA_OK : FA_ERR_DTYPE; }
+
+fa_status check_scale(float s) { return (isfinite(s) && s > 0.f) ? FA_OK : FA_ERR_SCALE; }
+
+fa_status check_mask(const uint8_t* m, int mb) { return (m != nullptr && mb != 128) ? FA_ERR_MASK : FA_OK; }
+
+#define FA_TRY(x)                     \
+  do {                                \
+    fa_status s_ = (x);               \
+    if (s_ != FA_OK) return s_;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 int d, fa_dtype dt, float scale, int causal, const uint8_t* block_mask, int mask_block,
+                 void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  FA_TRY(check_shape(B, H, N, d));
+  FA_TRY(check_dtype(dt));
+  FA_TRY(check_mask(block_mask, mask_block));
+  FA_TRY(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.mask = block_mask;
+  p.B = B; p.H = H; p.N = N; p.D = d;
+  p.mask_tiles = (N + 127) / 128;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd");
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N, int d, fa_dtype dt,
+                            void* stream) {
+  if (!o || !dO || !D) return FA_ERR_NULL;
+  FA_TRY(check_shape(B, H, N, d));
+  FA_TRY(check_dtype(dt));
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(D)) return FA_ERR_ALIGN;
+  const long long rows = (long long)B * H * N;
+  return hip_status(fa::launch_bwd_preprocess(o, dO, D, rows, d, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)),
+                    "fa_bwd_preprocess");
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  return (size_t)4 * (size_t)B * (size_t)H * (size_t)N * (size_t)d;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* D,
+                 void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, fa_dtype dt,
+                 float scale, int causal, const uint8_t* block_mask, int mask_block, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+  FA_TRY(check_shape(B, H, N, d));
+  FA_TRY(check_dtype(dt));
+  FA_TRY(check_mask(block_mask, mask_block));
+  FA_TRY(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(D) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const long long n = (long long)B * H * (long long)N * d;
+  float* acc = static_cast<float*>(workspace);
+  FA_TRY(hip_status(fa::launch_fill_zero(acc, n, st), "fa_bwd (clear workspace)"));
+
+  fa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.Dvec = D;
+  p.dq_acc = acc; p.dk = dk; p.dv = dv;
+  p.mask = block_mask;
+  p.B = B; p.H = H; p.N = N; p.D = d;
+  p.mask_tiles = (N + 127) / 128;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  FA_TRY(hip_status(fa::launch_bwd(p, dt == FA_BF16, st), "fa_bwd"));
+  return hip_status(fa::launch_dq_convert(acc, dq, n, scale, dt == FA_BF16, st), "fa_bwd (dq convert)");
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H and N must be >= 1 and the tensor must fit the index range";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_F16 or FA_BF16";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_MASK: return "FA_ERR_MASK: block_mask requires mask_block == 128";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+  }
+  return "unknown fa_status";
+}
+
+}  // extern "C"

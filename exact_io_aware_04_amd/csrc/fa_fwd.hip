@@ -1,0 +1,255 @@
+// Fused attention forward for gfx950: O = softmax(scale * Q K^T) V and the row
+// log-sum-exp, without writing the N x N score or probability matrices.
+//
+// Method: page 1 ("FlashAttention：不减少一次注意力计算，为什么反而更快"), key design 1
+// (tiling + fusion) and key design 2 (mergeable online-softmax state); page 3
+// ("FlashAttention"), forward-process section (unnormalised accumulator O~,
+// one division by l at the end); page 2 ("FlashAttention 入门"), FA2 section
+// (grid over batch x heads x query blocks, no atomics in the forward) and FA4
+// section (rescale the running state only when the maximum moved enough).
+//
+// Work decomposition (one workgroup = NW waves = NW*32 query rows of one head):
+//   * each wave owns 32 query rows; their Q fragments stay in VGPRs for the
+//     whole key loop (B operand of S^T = K Q^T, contraction over d);
+//   * K/V tiles of BN keys are copied HBM -> registers -> LDS (double buffered,
+//     the next tile's global loads are in flight while the current one is used);
+//   * S^T is computed so that each lane owns ONE query and 16 keys per 32-key
+//     sub-tile: the row max needs one cross-half exchange, and the
+//     probabilities P^T are already laid out as the B operand of
+//     O^T = V^T P^T (contraction over keys); V^T comes from LDS with the
+//     gfx950 transpose read;
+//   * causal tiles strictly above the diagonal and block-mask zero tiles are
+//     never loaded; only diagonal / ragged tiles are masked element-wise.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// Rescale the running state only when the running maximum grows by more than
+// this (log2 units); between rescales probabilities stay below 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <class DT, int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
+  using T = typename DT::T;
+  using V8 = typename DT::V8;
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  constexpr int ROWB = D * 2;                 // bytes per K/V row
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = BN * ROWB;
+  constexpr int PER_T = BN * CPR / NT;        // chunks per thread per tensor
+  constexpr int KC = D / 16;                  // contraction chunks over d
+  constexpr int NS = BN / 32;                 // 32-key sub-tiles per tile
+  static_assert(PER_T * NT == BN * CPR, "tile copy split");
+  static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int bh = logical / p.q_blocks;
+  int qb = logical - bh * p.q_blocks;
+  if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
+  const int q0 = qb * BM;
+  const int qw = q0 + wave * 32 + l32;        // this lane's query row
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Qg = reinterpret_cast<const T*>(p.q) + hoff;
+  const T* __restrict__ Kg = reinterpret_cast<const T*>(p.k) + hoff;
+  const T* __restrict__ Vg = reinterpret_cast<const T*>(p.v) + hoff;
+
+  // ---- key-tile range and skipping
+  const int n_tiles = (N + BN - 1) / BN;
+  int j_end = n_tiles;
+  if (p.causal) {
+    const int last_q = min(q0 + BM, N) - 1;
+    j_end = min(n_tiles, last_q / BN + 1);
+  }
+  const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
+  auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
+  auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
+
+  // ---- Q fragments (B operand): lane holds Q[qw][16c + 8g .. +7]
+  V8 qf[KC];
+  {
+    const bool ok = qw < N;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Qg + (size_t)(ok ? qw : 0) * D + 8 * g);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 x = ok ? src[2 * c] : u32x4{0, 0, 0, 0};
+      qf[c] = as_v8<DT>(x);
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float m_run = -INFINITY;   // running max of scale*log2(e)*s (the reference point)
+  float l_run = 0.f;         // this lane's share of the row sum at m_run
+  const float c2 = p.scale_log2;
+
+  // ---- tile copy helpers
+  u32x4 kr[PER_T], vr[PER_T];
+  auto gload = [&](int j) {
+    const int k0 = j * BN;
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int idx = tid + u * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      const int key = k0 + r;
+      if (key < N) {
+        kr[u] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8);
+        vr[u] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8);
+      } else {
+        kr[u] = u32x4{0, 0, 0, 0};
+        vr[u] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* kt = smem + buf * 2 * TILE;
+    char* vt = kt + TILE;
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      const int idx = tid + u * NT;
+      const int r = idx / CPR, c = idx % CPR;
+      const int off = tile_off<ROWB>(r, c * 8);
+      lds_write16(kt, off, kr[u]);
+      lds_write16(vt, off, vr[u]);
+    }
+  };
+
+  int j = next_kept(0);
+  if (j < j_end) {
+    gload(j);
+    sstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+
+  while (j < j_end) {
+    const int jn = next_kept(j + 1);
+    if (jn < j_end) gload(jn);
+
+    const char* kt = smem + buf * 2 * TILE;
+    const char* vt = kt + TILE;
+    const int k0 = j * BN;
+
+    // S^T sub-tiles: rows = keys (k0 + 32 s + mrow), column = this lane's query
+    f32x16 s[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        V8 a = as_v8<DT>(lds_read16(kt, tile_off<ROWB>(32 * t + l32, 16 * c + 8 * g)));
+        s[t] = DT::mma(a, qf[c], s[t]);
+      }
+    }
+
+    const bool edge = (k0 + BN > N) || (p.causal && k0 + BN - 1 > q0);
+    if (edge) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * t + mrow(g, r);
+          if (key >= N || (p.causal && key > qw)) s[t][r] = -INFINITY;
+        }
+    }
+
+    // row maximum over this tile (raw scores; the scale is positive)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float m_tile = mx * c2;
+    const bool need = m_tile > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+      if (need) m_run = m_tile;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    // probabilities (relative to m_run), row-sum share, B operands of O^T += V^T P^T
+    V8 pb[NS][2];
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c2, -m_use));
+        l_run += e[r];
+      }
+      pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    }
+
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc) {
+        const int t = kc >> 1, h = kc & 1;
+        V8 a = tr_operand<DT, ROWB, 8>(vt, 32 * t + 16 * h + 4 * g, 32 * dt, lane);
+        acc[dt] = DT::mma(a, pb[t][h], acc[dt]);
+      }
+    }
+
+    if (jn < j_end) sstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    j = jn;
+  }
+
+  // ---- epilogue: O = O~ / l, LSE = m ln2 + ln l
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (qw < N) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hoff + (size_t)qw * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x2 w = pack4<DT>(acc[dt][4 * jj] * inv, acc[dt][4 * jj + 1] * inv,
+                              acc[dt][4 * jj + 2] * inv, acc[dt][4 * jj + 3] * inv);
+          *reinterpret_cast<u32x2*>(Og + 32 * dt + 8 * jj + 4 * g) = w;
+        }
+      if (g == 0) {
+        p.lse[(size_t)bh * N + qw] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
+      }
+    }
+  }
+}
+
+template <class DT, int D, int BN, int NW>
+static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t st) {
+  FwdParams p = p0;
+  constexpr int BM = NW * 32;
+  p.q_blocks = (p.N + BM - 1) / BM;
+  p.total_blocks = p.B * p.H * p.q_blocks;
+  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {
+  if (p.D == 64) {
+    return is_bf16 ? launch_fwd_t<BF16, 64, 128, 4>(p, st) : launch_fwd_t<F16, 64, 128, 4>(p, st);
+  }
+  return is_bf16 ? launch_fwd_t<BF16, 128, 64, 4>(p, st) : launch_fwd_t<F16, 128, 64, 4>(p, st);
+}
+
+}  // namespace fa

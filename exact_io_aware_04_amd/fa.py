@@ -1,0 +1,169 @@
+"""Python binding of libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: every step of the attention computation runs in the
+HIP kernels behind the C entry points. PyTorch provides device memory and the
+stream. There is no fallback: if the shared library is missing or fails to
+load, importing this module raises.
+
+The low-level functions keep the C names (`fa_fwd`, `fa_bwd_preprocess`,
+`fa_bwd`, `fa_bwd_workspace_bytes`, `fa_status_string`) and take integer
+device addresses. `forward` / `backward` are thin conveniences over torch
+tensors that allocate the outputs and call the same entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_F16 = 0
+FA_BF16 = 1
+FA_OK = 0
+STATUS = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
+    -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE",
+}
+EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string")
+
+
+def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime with the same SONAME as the system one.
+    # Importing torch first makes libfa.so bind to that already-loaded
+    # runtime; loading libfa.so first would map a second HIP/HSA runtime into
+    # the process, and the two then fight over the device.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+            "or python exact_io_aware_04_amd/build.py). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.restype = i
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_bwd_preprocess.restype = i
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i]
+    return lib
+
+
+_lib = _load()
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {fa_status_string(status)} ({status})")
+        self.status = status
+
+
+# ---------------------------------------------------------------------------
+# C entry points (same names and argument order as include/fa.h)
+# ---------------------------------------------------------------------------
+def fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, stream) -> int:
+    return _lib.fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, stream)
+
+
+def fa_bwd_preprocess(o, dO, D, B, H, N, d, dt, stream) -> int:
+    return _lib.fa_bwd_preprocess(o, dO, D, B, H, N, d, dt, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d) -> int:
+    return _lib.fa_bwd_workspace_bytes(B, H, N, d)
+
+
+def fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B, H, N, d, dt, scale, causal, block_mask,
+           mask_block, stream) -> int:
+    return _lib.fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B, H, N, d, dt, scale, causal,
+                       block_mask, mask_block, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _shape(q):
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("expected contiguous [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, block_mask=None,
+            mask_block: int = 128, out=None, lse=None, stream=None):
+    """Run fa_fwd on [B, H, N, d] torch tensors; returns (o, lse)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    for t in (k, v):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                _dt(q), float(scale), int(bool(causal)), _ptr(block_mask), mask_block, _stream(stream))
+    _check(st, "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = False, block_mask=None,
+             mask_block: int = 128, workspace=None, D=None, stream=None):
+    """Run fa_bwd_preprocess then fa_bwd; returns (dq, dk, dv, D)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = _dt(q)
+    s = _stream(stream)
+    if D is None:
+        D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), B, H, N, d, dt, s), "fa_bwd_preprocess")
+    if workspace is None:
+        nbytes = fa_bwd_workspace_bytes(B, H, N, d)
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, N, d, dt,
+                float(scale), int(bool(causal)), _ptr(block_mask), mask_block, s)
+    _check(st, "fa_bwd")
+    return dq, dk, dv, D

@@ -1,0 +1,102 @@
+/* fa.h — C ABI of the gfx950 fused attention library (libfa.so).
+ *
+ * The operation is exact scaled-dot-product attention, O = softmax(s Q K^T) V
+ * with s the softmax scale, computed per (batch, head) over rows of length d.
+ * Sources (web pages on FlashAttention, cited by title and section):
+ *   [P1] "FlashAttention：不减少一次注意力计算，为什么反而更快" (awesome.papernotes.org),
+ *        key design 1 (operator and tiling), key design 2 (mergeable softmax
+ *        state; the saved log-sum-exp L = m + log l), key design 3 (backward by
+ *        recomputation, D_i = dO_i . O_i, dS = P o (dP - D)), IO section
+ *        (block-sparse variant: zero blocks skipped, exact inside kept blocks).
+ *   [P2] "FlashAttention 入门：从 FA1 到 FA4 的 IO 感知注意力" (oripoin.cn),
+ *        FA1 section (causal: keys j > i skipped or masked), backward section
+ *        (dQ accumulated with atomic adds; the default backward is not bitwise
+ *        deterministic while the forward is).
+ *   [P3] "FlashAttention" (lyirs.cc), forward-process section (unnormalised
+ *        accumulator, one final division by l).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates nothing, keeps no state, and returns without synchronising.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Tensors q, k, v, o, dO, dq, dk, dv are contiguous [B, H, N, d] with d
+ *     fastest, 16-bit elements of type `dt`. lse and D are contiguous
+ *     [B, H, N] float32. Pointers must be 16-byte aligned.
+ *   - Attention is square self-attention (N queries, N keys per head).
+ *   - causal != 0 keeps key j for query i only when j <= i [P2, FA1 section].
+ *   - block_mask, when not NULL, is a row-major uint8 [T, T] tile mask with
+ *     T = ceil(N / mask_block), shared by every (batch, head); tile (a, b)
+ *     nonzero keeps queries a*mask_block.. with keys b*mask_block..; zero
+ *     tiles are skipped [P1, IO section]. mask_block must be 128. causal and
+ *     block_mask combine with a logical AND. A masked pair is -inf before the
+ *     softmax: each row normalises over its kept keys only. A row with no
+ *     kept key yields O = 0 and LSE = -inf and receives no gradient.
+ *   - scale is the softmax scale s (callers normally pass 1/sqrt(d)); it must
+ *     be finite and > 0.
+ *   - Outputs must not alias inputs. Arguments are validated before any HIP
+ *     call; on a validation error nothing is enqueued. Asynchronous device
+ *     faults surface at the caller's next synchronisation, as with any HIP
+ *     library.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,     /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, or B*H*N*d does not fit the 64-bit index range */
+  FA_ERR_DTYPE = -3,    /* dt is not FA_F16 or FA_BF16 */
+  FA_ERR_HEADDIM = -4,  /* d is not 64 or 128 */
+  FA_ERR_MASK = -5,     /* block_mask given with mask_block != 128 */
+  FA_ERR_ALIGN = -6,    /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_HIP = -7,      /* a HIP launch reported an error */
+  FA_ERR_SCALE = -8     /* scale is not finite and > 0 */
+} fa_status;
+
+/* Forward [P1 key designs 1-2; P3 forward process].
+ * Writes o = softmax(scale * q k^T) v, rounded to dt (round to nearest even),
+ * and lse[b,h,i] = ln sum_j exp(scale * q_i . k_j) over kept keys (float32,
+ * natural log of the scaled scores). Deterministic: identical inputs give
+ * identical bits. No N x N buffer is used. */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
+                 const uint8_t* block_mask, int mask_block, void* stream);
+
+/* Backward preprocess [P1 key design 3]: D[b,h,i] = sum_c dO[b,h,i,c] * o[b,h,i,c],
+ * products and sum in float32, using the stored 16-bit o from fa_fwd. */
+fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D,
+                            int B, int H, int N, int d, fa_dtype dt, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: 4*B*H*N*d (the float32 dQ accumulator).
+ * Returns 0 for invalid shapes. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward by recomputation [P1 key design 3; P2 backward section].
+ * Inputs: q, k, v, dO (the gradient of o), lse from fa_fwd and D from
+ * fa_bwd_preprocess, with the same shape, scale, causal flag and mask as the
+ * forward. Writes dq, dk, dv (dt, rounded to nearest even). `workspace`
+ * (caller-owned, at least fa_bwd_workspace_bytes, 16-byte aligned) is cleared
+ * and used as a float32 dQ accumulator. dq is summed with float32 atomic adds,
+ * so its low bits may differ between runs; dk and dv are deterministic. */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO,
+                 const float* lse, const float* D, void* dq, void* dk, void* dv,
+                 void* workspace, int B, int H, int N, int d, fa_dtype dt, float scale,
+                 int causal, const uint8_t* block_mask, int mask_block, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -137,39 +137,49 @@ def backward_head(q, k, v, do, scale: float, causal: bool = False,
 def backward_head_sampled(q, k, v, do, scale: float, causal: bool,
                           block_mask: Optional[np.ndarray], mask_block: int,
                           q_rows: Sequence[int], k_rows: Sequence[int],
-                          row_block: int = 1024):
+                          first_row: int = 0, row_block: int = 1024):
     """Gradients at selected indices for a head too large to differentiate whole.
 
-    Needs the full-row statistics first: LSE_i and O_i for every query (the
-    plain forward), then D_i = sum_k dO_ik O_ik (equal to sum_j P_ij dP_ij,
-    the D identity). With those, dQ at a query row needs only that row of P,
-    and dK, dV at a key row need only that column of P:
+    dQ at a query row needs only that row of P plus D_i = sum_k dO_ik O_ik
+    (equal to sum_j P_ij dP_ij, the D identity), all computable from that row:
       dQ_i = scale sum_j P_ij (dP_ij - D_i) K_j
+    dK, dV at a key column j need that column of P, hence LSE_i and D_i of
+    every query row that sees key j:
       dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i P_ij (dP_ij - D_i) Q_i
+    `first_row` > 0 restricts those rows to i >= first_row; that is exact
+    only for causal attention with every sampled key index >= first_row
+    (P_ij = 0 for i < j), which is asserted.
     Returns (dQ[q_rows], dK[k_rows], dV[k_rows], D[q_rows]).
     """
     n = k.shape[0]
-    o, lse = forward_head(q, k, v, scale, causal, block_mask, mask_block, row_block=row_block)
-    dd = (do * o).sum(axis=1)
-    live = np.isfinite(lse)
-    lse_safe = np.where(live, lse, 0.0)
     q_rows = np.asarray(q_rows, dtype=np.int64)
     k_rows = np.asarray(k_rows, dtype=np.int64)
+    if first_row > 0:
+        assert causal and k_rows.size and k_rows.min() >= first_row
     all_idx = np.arange(n)
 
+    o_q, lse_q = forward_head(q, k, v, scale, causal, block_mask, mask_block, rows=q_rows,
+                              row_block=row_block)
+    dd_q = (do[q_rows] * o_q).sum(axis=1)
+    live_q = np.isfinite(lse_q)
     keep = kept_pairs(q_rows, all_idx, causal, block_mask, mask_block)
     s = _scores(q[q_rows], k, scale, keep)
-    p = np.where(live[q_rows, None], np.exp(s - lse_safe[q_rows, None]), 0.0)
+    p = np.where(live_q[:, None], np.exp(s - np.where(live_q, lse_q, 0.0)[:, None]), 0.0)
     dp = do[q_rows] @ v.T
-    dq = scale * ((p * (dp - dd[q_rows, None])) @ k)
+    dq = scale * ((p * (dp - dd_q[:, None])) @ k)
 
-    keep_t = kept_pairs(all_idx, k_rows, causal, block_mask, mask_block)   # [N, K]
-    s_t = np.where(keep_t, scale * (q @ k[k_rows].T), -np.inf)
-    p_t = np.where(live[:, None], np.exp(s_t - lse_safe[:, None]), 0.0)
-    dp_t = do @ v[k_rows].T
-    dv = p_t.T @ do
-    dk = scale * ((p_t * (dp_t - dd[:, None])).T @ q)
-    return dq, dk, dv, dd[q_rows]
+    rows = np.arange(first_row, n)
+    o_r, lse_r = forward_head(q, k, v, scale, causal, block_mask, mask_block, rows=rows,
+                              row_block=row_block)
+    dd_r = (do[rows] * o_r).sum(axis=1)
+    live_r = np.isfinite(lse_r)
+    keep_t = kept_pairs(rows, k_rows, causal, block_mask, mask_block)       # [R, K]
+    s_t = np.where(keep_t, scale * (q[rows] @ k[k_rows].T), -np.inf)
+    p_t = np.where(live_r[:, None], np.exp(s_t - np.where(live_r, lse_r, 0.0)[:, None]), 0.0)
+    dp_t = do[rows] @ v[k_rows].T
+    dv = p_t.T @ do[rows]
+    dk = scale * ((p_t * (dp_t - dd_r[:, None])).T @ q[rows])
+    return dq, dk, dv, dd_q
 
 
 # ---------------------------------------------------------------------------

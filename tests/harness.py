@@ -1,0 +1,111 @@
+"""GPU-test helpers: move seeded 16-bit inputs to the device, run the C ABI
+through the Python binding, bring results back as float64, and compare with
+the oracle under the stated tolerances.
+
+Tolerances (written here once, used by every parity test):
+  * O: max |GPU - oracle| <= 2e-3 for fp16, <= 1e-2 for bf16.
+  * dQ, dK, dV: ||GPU - oracle||_F / ||oracle||_F <= 2e-2 per tensor.
+  * LSE: max |GPU - oracle| <= 2e-3 on rows with a visible key; rows without
+    one must be -inf on both sides. (The fp32 log-sum-exp carries relative
+    error ~1e-7 of |m| plus the log approximation; 2e-3 is loose.)
+  * D (preprocess): max |GPU - sum(dO * O_gpu)| <= 1e-3 * (1 + |D|), computed
+    from the GPU's own stored O, which is what the preprocess reads.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import attn_inputs as ai
+
+O_TOL = {ai.F16: 2e-3, ai.BF16: 1e-2}
+GRAD_REL_TOL = 2e-2
+LSE_TOL = 2e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float16 if dtype == ai.F16 else torch.bfloat16
+
+
+def to_dev(bits: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch_dtype(dtype)).cuda()
+
+
+def from_dev(t, dtype: str) -> np.ndarray:
+    import torch
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return ai.bits_to_f64(bits, dtype)
+
+
+def mask_dev(mask):
+    import torch
+    if mask is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
+
+
+def run_gpu(dr: ai.Drawn, scale: float, causal: bool, mask=None, backward: bool = True, poison: bool = True):
+    """fa_fwd (+ fa_bwd_preprocess, fa_bwd) on the drawn inputs. Returns float64 numpy arrays."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    q, k, v = (to_dev(getattr(dr, n), dr.dtype) for n in "qkv")
+    bm = mask_dev(mask)
+    B, H, N, d = dr.q.shape
+    o = torch.full_like(q, float("nan")) if poison else None
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=q.device) if poison else None
+    o, lse = fa.forward(q, k, v, scale, causal, bm, out=o, lse=lse)
+    out = {"o_dev": o, "lse_dev": lse}
+    if backward:
+        do = to_dev(dr.do, dr.dtype)
+        dq, dk, dv, D = fa.backward(q, k, v, o, lse, do, scale, causal, bm)
+        out.update(dq=dq, dk=dk, dv=dv, D=D)
+    torch.cuda.synchronize()
+    res = {"o": from_dev(o, dr.dtype), "lse": lse.double().cpu().numpy()}
+    if backward:
+        for n in ("dq", "dk", "dv"):
+            res[n] = from_dev(out[n], dr.dtype)
+        res["D"] = out["D"].double().cpu().numpy()
+    return res
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    nb = float(np.linalg.norm(b))
+    na = float(np.linalg.norm(a - b))
+    return na / nb if nb > 0 else na
+
+
+def check_forward(o, lse, o_ref, lse_ref, dtype, what=""):
+    assert np.isfinite(o).all(), f"{what}: non-finite O (unwritten output?)"
+    err = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    assert err <= O_TOL[dtype], f"{what}: O max-abs error {err:.3e} > {O_TOL[dtype]}"
+    live = np.isfinite(lse_ref)
+    assert (np.isneginf(lse) == ~live).all(), f"{what}: LSE -inf pattern differs"
+    lerr = float(np.abs(lse[live] - lse_ref[live]).max()) if live.any() else 0.0
+    assert lerr <= LSE_TOL, f"{what}: LSE max-abs error {lerr:.3e}"
+    return err, lerr
+
+
+def check_grads(res, ref, what=""):
+    errs = {}
+    for n in ("dq", "dk", "dv"):
+        g, r = res[n], ref[n]
+        assert np.isfinite(g).all(), f"{what}: non-finite {n}"
+        e = rel_fro(g, r)
+        errs[n] = e
+        assert e <= GRAD_REL_TOL, f"{what}: {n} relative error {e:.3e} > {GRAD_REL_TOL}"
+    return errs
+
+
+def check_D(D, do, o_gpu, what=""):
+    ref = (do * o_gpu).sum(axis=-1)
+    err = float((np.abs(D - ref) / (1 + np.abs(ref))).max())
+    assert err <= 1e-3, f"{what}: D error {err:.3e}"

@@ -1,0 +1,112 @@
+"""C ABI: the library loads, exports every declared symbol, and validates its
+arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_io_aware_04_amd.fa", reason="libfa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fa_[a-z_0-9]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    for code, name in fa.STATUS.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert "unknown" in fa.fa_status_string(123)
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100, 64) == 4 * 2 * 3 * 100 * 64
+    assert fa.fa_bwd_workspace_bytes(1, 8, 65536, 128) == 4 * 8 * 65536 * 128
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 10, 96) == 0
+
+
+# Fake, never-dereferenced addresses: validation rejects before any HIP call.
+A = 1 << 20          # 16-byte aligned
+MIS = A + 8          # misaligned
+
+
+def fwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=16, d=64, dt=fa.FA_F16, scale=0.125, causal=0,
+                block_mask=None, mask_block=128, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(*args.values())
+
+
+def bwd(**kw):
+    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, workspace=A, B=1, H=1, N=16, d=64,
+                dt=fa.FA_F16, scale=0.125, causal=0, block_mask=None, mask_block=128, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2), (dict(B=1 << 20, H=1 << 10, N=1 << 20), -2),
+    (dict(dt=2), -3), (dict(dt=-1), -3),
+    (dict(d=32), -4), (dict(d=96), -4), (dict(d=256), -4),
+    (dict(block_mask=A, mask_block=64), -5),
+    (dict(q=MIS), -6), (dict(lse=MIS), -6),
+    (dict(scale=0.0), -8), (dict(scale=-1.0), -8), (dict(scale=float("inf")), -8), (dict(scale=float("nan")), -8),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(workspace=None), -1), (dict(D=None), -1), (dict(dv=None), -1),
+    (dict(N=0), -2), (dict(dt=7), -3), (dict(d=80), -4),
+    (dict(block_mask=A, mask_block=256), -5),
+    (dict(workspace=MIS), -6), (dict(dq=MIS), -6),
+    (dict(scale=0.0), -8),
+])
+def test_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_preprocess_validation():
+    assert fa.fa_bwd_preprocess(None, A, A, 1, 1, 16, 64, 0, None) == -1
+    assert fa.fa_bwd_preprocess(A, A, A, 1, 1, 0, 64, 0, None) == -2
+    assert fa.fa_bwd_preprocess(A, A, A, 1, 1, 16, 64, 5, None) == -3
+    assert fa.fa_bwd_preprocess(A, A, A, 1, 1, 16, 48, 0, None) == -4
+    assert fa.fa_bwd_preprocess(A, MIS, A, 1, 1, 16, 64, 0, None) == -6
+
+
+def test_binding_keeps_a_single_hip_runtime():
+    """The binding loads torch's HIP runtime before libfa.so, so only one
+    libamdhip64 / libhsa-runtime64 is mapped, whatever is imported first."""
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from exact_io_aware_04_amd import fa\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read().splitlines()\n"
+        "libs = {l.split()[-1] for l in maps if 'amdhip64' in l or 'hsa-runtime64' in l}\n"
+        "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime64' in x]))\n"
+    ) % ROOT
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["1", "1"], out.stdout

@@ -1,0 +1,204 @@
+"""HIP path vs the float64 oracle, through the C ABI (Python binding).
+
+Small shapes span several tiles and ragged tails and are compared element by
+element; the five full-size workloads run in the launch configuration the
+benchmark times and are compared on whole sampled heads, sampled rows /
+columns, and invariants that hold at any size. Every GPU step prints its case
+first so that a failure names it.
+"""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from harness import (GRAD_REL_TOL, check_D, check_forward, check_grads, from_dev, rel_fro, run_gpu,
+                     say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_N = [1, 17, 64, 127, 128, 129, 255, 256, 1000]
+MODES = ["dense", "causal", "mask", "causal_mask"]
+
+
+def _mask_for(mode, n, seed):
+    if "mask" not in mode:
+        return None
+    return ai.random_block_mask(-(-n // 128), 0.5, seed)
+
+
+def _oracle_head(dr, b, h, scale, causal, mask, backward=True):
+    q, k, v = (dr.f64(n, b, h) for n in "qkv")
+    o, lse = oracle.forward_head(q, k, v, scale, causal, mask, 128)
+    out = {"o": o, "lse": lse}
+    if backward:
+        do = dr.f64("do", b, h)
+        out["dq"], out["dk"], out["dv"], out["D"] = oracle.backward_head(q, k, v, do, scale, causal, mask, 128)
+    return out
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", [ai.F16, ai.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", SMALL_N)
+def test_small_shapes(n, d, dtype, mode):
+    causal = "causal" in mode
+    seed = 10_000 + 97 * n + d + (1 if dtype == ai.BF16 else 0) + 7 * MODES.index(mode)
+    mask = _mask_for(mode, n, seed)
+    say(f"[small] N={n} d={d} {dtype} {mode} seed={seed}")
+    dr = ai.draw(1, 2, n, d, dtype, seed)
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, causal, mask, backward=True)
+    o_dev = res["o"]
+    for h in range(2):
+        ref = _oracle_head(dr, 0, h, scale, causal, mask)
+        what = f"N={n} d={d} {dtype} {mode} h={h}"
+        check_forward(res["o"][0, h], res["lse"][0, h], ref["o"], ref["lse"], dtype, what)
+        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
+        check_D(res["D"][0, h], dr.f64("do", 0, h), o_dev[0, h], what)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [ai.F16, ai.BF16])
+def test_fully_masked_rows(causal, dtype):
+    """Rows whose tiles are all masked: O = 0, LSE = -inf, no gradient (reading R8b)."""
+    n, d = 300, 64
+    mask = np.array([[1, 0, 0], [0, 0, 0], [1, 1, 1]], dtype=np.uint8)
+    say(f"[masked rows] causal={causal} {dtype}")
+    dr = ai.draw(1, 1, n, d, dtype, 4242)
+    scale = 0.125
+    res = run_gpu(dr, scale, causal, mask)
+    ref = _oracle_head(dr, 0, 0, scale, causal, mask)
+    check_forward(res["o"][0, 0], res["lse"][0, 0], ref["o"], ref["lse"], dtype, "masked rows")
+    assert (res["o"][0, 0, 128:256] == 0).all()
+    check_grads({k: res[k][0, 0] for k in ("dq", "dk", "dv")}, ref, "masked rows")
+    assert (res["dq"][0, 0, 128:256] == 0).all()
+
+
+def test_forward_is_bitwise_deterministic():
+    import torch
+    from exact_io_aware_04_amd import fa
+    say("[determinism] N=1000 d=128 bf16 causal x3")
+    dr = ai.draw(2, 4, 1000, 128, ai.BF16, 77, with_do=False)
+    q, k, v = (to_dev(getattr(dr, n), dr.dtype) for n in "qkv")
+    outs = [fa.forward(q, k, v, 0.09, True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Canaries around every output buffer; raw C entry points with sliced pointers."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    B, H, n, d = 1, 2, 200, 64
+    say("[canary] N=200 d=64 f16 causal")
+    dr = ai.draw(B, H, n, d, ai.F16, 91)
+    q, k, v, do = (to_dev(getattr(dr, x), dr.dtype) for x in ("q", "k", "v", "do"))
+    numel = B * H * n * d
+    PAD = 64
+    def guarded(count, dtype):
+        buf = torch.full((count + 2 * PAD,), 7.0, dtype=dtype, device="cuda")
+        return buf, buf[PAD:PAD + count]
+    ob, o = guarded(numel, torch.float16)
+    lb, lse = guarded(B * H * n, torch.float32)
+    Db, D = guarded(B * H * n, torch.float32)
+    qb_, dq = guarded(numel, torch.float16)
+    kb_, dk = guarded(numel, torch.float16)
+    vb_, dv = guarded(numel, torch.float16)
+    wb, ws = guarded(numel, torch.float32)
+    s = torch.cuda.current_stream().cuda_stream
+    assert fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d,
+                     fa.FA_F16, 0.125, 1, None, 128, s) == 0
+    assert fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), D.data_ptr(), B, H, n, d, fa.FA_F16, s) == 0
+    assert fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, n, d, fa.FA_F16,
+                     0.125, 1, None, 128, s) == 0
+    torch.cuda.synchronize()
+    for buf in (ob, lb, Db, qb_, kb_, vb_, wb):
+        assert (buf[:PAD] == 7.0).all() and (buf[-PAD:] == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (the benchmark's launch configuration)
+# ---------------------------------------------------------------------------
+def _full_run(name):
+    w = ai.WORKLOADS[name]
+    say(f"[full] {name}: drawing inputs")
+    dr = ai.draw_workload(w)
+    mask = w.block_mask()
+    say(f"[full] {name}: GPU fwd{'+bwd' if w.backward else ''}")
+    res = run_gpu(dr, w.scale, w.causal, mask, backward=w.backward)
+    return w, dr, mask, res
+
+
+def test_full_single_head_forward():
+    w, dr, mask, res = _full_run("single_head_fwd_n256_d64_f16")
+    ref = _oracle_head(dr, 0, 0, w.scale, w.causal, mask, backward=False)
+    check_forward(res["o"][0, 0], res["lse"][0, 0], ref["o"], ref["lse"], w.dtype, w.name)
+
+
+def test_full_gpt2_medium_shape():
+    w, dr, mask, res = _full_run("gpt2_medium_b64_h16_n1024_d64_f16")
+    rng = np.random.Generator(np.random.PCG64(5))
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [tuple(x) for x in rng.integers(0, [w.B, w.H], size=(6, 2))]
+    for b, h in heads:
+        say(f"[full] {w.name}: oracle head ({b},{h})")
+        ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
+        what = f"{w.name} head ({b},{h})"
+        check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
+        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+    assert np.isfinite(res["o"]).all() and np.isfinite(res["dq"]).all()
+
+
+def test_full_causal_8k():
+    w, dr, mask, res = _full_run("causal_b2_h32_n8192_d128_bf16")
+    for b, h in [(0, 0), (1, 31)]:
+        say(f"[full] {w.name}: oracle head ({b},{h})")
+        ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
+        what = f"{w.name} head ({b},{h})"
+        check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
+        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.isfinite(res[n]).all()
+
+
+def test_full_butterfly_16k():
+    w, dr, mask, res = _full_run("butterfly_b4_h16_n16384_d64_f16")
+    for b, h in [(3, 5)]:
+        say(f"[full] {w.name}: oracle head ({b},{h})")
+        ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
+        what = f"{w.name} head ({b},{h})"
+        check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
+        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.isfinite(res[n]).all()
+
+
+def test_full_causal_64k_sampled():
+    """N = 65536: whole heads are out of the oracle's reach; compare sampled
+    rows of O/LSE/dQ, sampled late key columns of dK/dV, and two invariants
+    over every key of the head (sum_j dV_j = sum_i dO_i, sum_j dK_j = 0)."""
+    w, dr, mask, res = _full_run("causal_b1_h8_n65536_d128_bf16")
+    N = w.N
+    rng = np.random.Generator(np.random.PCG64(11))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, N // 2, N - 129, N - 1],
+                                     rng.integers(0, N, 56)]))
+    cols = np.unique(np.concatenate([[N - 1, N - 128, N - 129, N - 2048],
+                                     rng.integers(N - 2048, N, 28)]))
+    for h in (0, 7):
+        say(f"[full] {w.name}: oracle rows/cols head {h}")
+        q, k, v, do = (dr.f64(n, 0, h) for n in ("q", "k", "v", "do"))
+        o_ref, lse_ref = oracle.forward_head(q, k, v, w.scale, True, None, 128, rows=rows)
+        check_forward(res["o"][0, h, rows], res["lse"][0, h, rows], o_ref, lse_ref, w.dtype, f"{w.name} h{h}")
+        dq, dk, dv, _ = oracle.backward_head_sampled(q, k, v, do, w.scale, True, None, 128, rows, cols,
+                                                     first_row=N - 2048)
+        check_grads({"dq": res["dq"][0, h, rows], "dk": res["dk"][0, h, cols], "dv": res["dv"][0, h, cols]},
+                    {"dq": dq, "dk": dk, "dv": dv}, f"{w.name} h{h} sampled")
+        # invariants over the whole head (hold for any N)
+        sum_dv, sum_do = res["dv"][0, h].sum(axis=0), do.sum(axis=0)
+        assert rel_fro(sum_dv, sum_do) <= GRAD_REL_TOL
+        sum_dk = res["dk"][0, h].sum(axis=0)
+        assert np.linalg.norm(sum_dk) <= 1e-2 * np.abs(res["dk"][0, h]).sum(axis=0).max()
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.isfinite(res[n]).all()

@@ -372,6 +372,14 @@ def test_sampled_backward_matches_whole_head(causal, masked):
     np.testing.assert_allclose(sk, dk[cols], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(sv, dv[cols], rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(sd, D[rows], rtol=1e-11, atol=1e-12)
+    if causal:
+        late = np.array([40, 47, 63])
+        tq, tk, tv, _ = oracle.backward_head_sampled(q, k, v, g, 0.35, causal, bm, bs, rows, late,
+                                                     first_row=40)
+        np.testing.assert_allclose(tk, dk[late], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(tv, dv[late], rtol=1e-11, atol=1e-12)
+        with pytest.raises(AssertionError):
+            oracle.backward_head_sampled(q, k, v, g, 0.35, causal, bm, bs, rows, cols, first_row=40)
 
 
 def test_batched_helpers_loop_over_heads():
