@@ -21,9 +21,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 fa_status check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  // element count must fit comfortably in signed 64-bit and grid dims in 31 bits
+  // element count must fit comfortably in signed 64-bit
   const long double elems = (long double)B * H * (long double)N * d;
   if (elems > 9.0e18L) return FA_ERR_SHAPE;
+  // byte offsets inside one head (fp32 dQ accumulator included) are 32-bit
+  if ((long long)N * d * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
   // the dispatch grid counts work-items in 32 bits: blocks * 256 threads < 2^32
   const long double blocks = (long double)B * H * ((N + 31) / 32 + 1);
   if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;

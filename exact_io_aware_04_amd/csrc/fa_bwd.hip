@@ -75,8 +75,11 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // Main backward kernel
 // ---------------------------------------------------------------------------
+template <int D>
+struct BwdOccupancy { static constexpr int value = D <= 64 ? 2 : 1; };
+
 template <class DT, int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
   constexpr int NT = NW * 64;
@@ -84,27 +87,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int QTILE = BQ * ROWB;
-  constexpr int KTILE = BK * ROWB;
   constexpr int SROWB = BQ * 2;               // dS^T rows: keys, columns: queries
   constexpr int STILE = BK * SROWB;
   constexpr int KC = D / 16;
-  constexpr int MQ = BQ / 32;                 // 32-query blocks per tile
+  constexpr int MQ = BQ / 32;                 // 32-query halves per tile
+  constexpr int DT32 = D / 32;
   constexpr int PER_T = BQ * CPR / NT;        // Q/dO chunks per thread
   constexpr int KPER_T = BK * CPR / NT;
-  constexpr int DQ_TILES = MQ * (D / 32);
+  constexpr int DQ_TILES = MQ * DT32;
   constexpr int DQ_PER_WAVE = DQ_TILES / NW;
   static_assert(PER_T * NT == BQ * CPR && KPER_T * NT == BK * CPR, "copy split");
   static_assert(DQ_PER_WAVE * NW == DQ_TILES && DQ_PER_WAVE >= 1, "dQ split");
+  static_assert(NW % DT32 == 0 || DT32 % NW == 0, "dQ tiles per wave share one head-dim block");
   static_assert(BK == 128 && 128 % BQ == 0, "block-mask granularity");
+  static_assert(2 * QTILE >= BK * ROWB, "K staging fits the second Q/dO buffer pair");
 
-  // [Q buf0|Q buf1|dO buf0|dO buf1|K|dS^T|lse2 x2|D x2]
-  __shared__ __attribute__((aligned(16))) char smem[4 * QTILE + KTILE + STILE + 4 * BQ * 4];
-  char* const q_s = smem;
-  char* const do_s = smem + 2 * QTILE;
-  char* const k_s = smem + 4 * QTILE;
-  char* const ds_s = k_s + KTILE;
+  // [Q buf0 | dO buf0 | Q buf1 | dO buf1 | dS^T | lse2 x2 | D x2]; the K tile is
+  // staged once in the buf1 pair before the first Q/dO tile lands there.
+  __shared__ __attribute__((aligned(16))) char smem[4 * QTILE + STILE + 4 * BQ * 4];
+  char* const ds_s = smem + 4 * QTILE;
   float* const lse_s = reinterpret_cast<float*>(ds_s + STILE);   // [2][BQ]
   float* const dd_s = lse_s + 2 * BQ;                              // [2][BQ]
+  char* const k_s = smem + 2 * QTILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -114,38 +118,48 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
   const int bh = logical / p.k_blocks;
   const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
   const int k0 = kb * BK;
-  const int kw = k0 + wave * 32 + l32;        // this lane's key (column of S, dP)
+  const int kw0 = k0 + wave * 32;
+  const int kw = kw0 + l32;                   // this lane's key (column of S and dP)
 
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Qg = reinterpret_cast<const T*>(p.q) + hoff;
-  const T* __restrict__ Kg = reinterpret_cast<const T*>(p.k) + hoff;
-  const T* __restrict__ Vg = reinterpret_cast<const T*>(p.v) + hoff;
-  const T* __restrict__ dOg = reinterpret_cast<const T*>(p.dO) + hoff;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
+  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
+  const auto dq_rs = make_rsrc(p.dq_acc + hoff, (uint32_t)N * D * 4);
   const float* __restrict__ lse_g = p.lse + (size_t)bh * N;
   const float* __restrict__ D_g = p.Dvec + (size_t)bh * N;
-  float* __restrict__ dq_g = p.dq_acc + hoff;
 
-  // ---- K, V fragments (B operands): lane holds K[kw][16c + 8g .. +7]
+  // ---- K, V fragments (B operands of S = Q K^T and dP = dO V^T); keys >= N read as zero
   V8 kf[KC], vf[KC];
-  {
-    const bool ok = kw < N;
-    const u32x4* ks = reinterpret_cast<const u32x4*>(Kg + (size_t)(ok ? kw : 0) * D + 8 * g);
-    const u32x4* vs = reinterpret_cast<const u32x4*>(Vg + (size_t)(ok ? kw : 0) * D + 8 * g);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      kf[c] = as_v8<DT>(ok ? ks[2 * c] : u32x4{0, 0, 0, 0});
-      vf[c] = as_v8<DT>(ok ? vs[2 * c] : u32x4{0, 0, 0, 0});
-    }
+  for (int c = 0; c < KC; ++c) {
+    kf[c] = as_v8<DT>(buf_load16(k_rs, (kw * D + 16 * c + 8 * g) * 2));
+    vf[c] = as_v8<DT>(buf_load16(v_rs, (kw * D + 16 * c + 8 * g) * 2));
   }
-  // ---- K tile in LDS (B operand of dQ = dS K, read transposed)
+  // ---- K tile to LDS, read back transposed as the B operand of dQ = dS K
 #pragma unroll
   for (int u = 0; u < KPER_T; ++u) {
     const int idx = tid + u * NT;
     const int r = idx / CPR, c = idx % CPR;
-    const int key = k0 + r;
-    u32x4 x = key < N ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
-    lds_write16(k_s, tile_off<ROWB>(r, c * 8), x);
+    lds_write16(k_s, tile_off<ROWB>(r, 8 * c), buf_load16(k_rs, ((k0 + r) * D + 8 * c) * 2));
   }
+
+  // ---- lane-constant LDS offsets
+  int qoff[KC];                               // Q / dO operand rows l32, chunk 2c + g
+#pragma unroll
+  for (int c = 0; c < KC; ++c) qoff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
+  int troff[DT32];                            // dO^T / Q^T operands: rows 4g + (lane%16)/4 (+ block base)
+#pragma unroll
+  for (int d0 = 0; d0 < DT32; ++d0) troff[d0] = tr_off<ROWB>(4 * g, 32 * d0, lane);
+  // dQ work of this wave: head-dim block dq_d0, query halves dq_mq0 .. dq_mq0 + DQ_PER_WAVE - 1
+  const int dq_d0 = wave % DT32;
+  const int dq_mq0 = (wave / DT32) * DQ_PER_WAVE;
+  // (a column shift is not additive under the row swizzle, so one offset per tile)
+  int dsoff[DQ_PER_WAVE];
+#pragma unroll
+  for (int w = 0; w < DQ_PER_WAVE; ++w) dsoff[w] = tr_off<SROWB>(4 * g, 32 * (dq_mq0 + w), lane);
 
   // ---- query-tile range and skipping
   const int n_qt = (N + BQ - 1) / BQ;
@@ -154,25 +168,25 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
   auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
   auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
 
+  int goff[PER_T], soff[PER_T];
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {
+    const int idx = tid + u * NT;
+    const int r = idx / CPR, c = idx % CPR;
+    goff[u] = (r * D + 8 * c) * 2;
+    soff[u] = tile_off<ROWB>(r, 8 * c);
+  }
   u32x4 qr[PER_T], dr[PER_T];
   float lse_r = 0.f, dd_r = 0.f;
   auto gload = [&](int i) {
-    const int q0 = i * BQ;
+    const int base = i * BQ * D * 2;          // rows >= N read as zero
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int q = q0 + r;
-      if (q < N) {
-        qr[u] = *reinterpret_cast<const u32x4*>(Qg + (size_t)q * D + c * 8);
-        dr[u] = *reinterpret_cast<const u32x4*>(dOg + (size_t)q * D + c * 8);
-      } else {
-        qr[u] = u32x4{0, 0, 0, 0};
-        dr[u] = u32x4{0, 0, 0, 0};
-      }
+      qr[u] = buf_load16(q_rs, goff[u] + base);
+      dr[u] = buf_load16(do_rs, goff[u] + base);
     }
     if (tid < BQ) {
-      const int q = q0 + tid;
+      const int q = i * BQ + tid;
       const float l = q < N ? lse_g[q] : -INFINITY;
       // rows past N or with no visible key get P = exp2(s - inf) = 0
       lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
@@ -180,13 +194,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
     }
   };
   auto sstore = [&](int buf) {
+    char* qt = smem + buf * 2 * QTILE;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int off = tile_off<ROWB>(r, c * 8);
-      lds_write16(q_s + buf * QTILE, off, qr[u]);
-      lds_write16(do_s + buf * QTILE, off, dr[u]);
+      lds_write16(qt, soff[u], qr[u]);
+      lds_write16(qt + QTILE, soff[u], dr[u]);
     }
     if (tid < BQ) {
       lse_s[buf * BQ + tid] = lse_r;
@@ -194,9 +206,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
     }
   };
 
-  f32x16 dv[D / 32], dk[D / 32];
+  f32x16 dv[DT32], dk[DT32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) { dv[t] = f32x16{}; dk[t] = f32x16{}; }
+  for (int t = 0; t < DT32; ++t) { dv[t] = f32x16{}; dk[t] = f32x16{}; }
 
   const float c2 = p.scale_log2;
   int i = next_kept(i_begin);
@@ -205,28 +217,32 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
     sstore(0);
   }
   __syncthreads();
+  V8 ktf[BK / 16];                            // K[keys of chunk kc][dim 32 dq_d0 + l32]
+  {
+    const int koff = tr_off<ROWB>(4 * g, 32 * dq_d0, lane);
+#pragma unroll
+    for (int kc = 0; kc < BK / 16; ++kc) ktf[kc] = tr_pair<DT>(k_s, koff + 16 * kc * ROWB, 8 * ROWB);
+  }
   int buf = 0;
 
   while (i < n_qt) {
     const int in = next_kept(i + 1);
     if (in < n_qt) gload(in);
     const int q0 = i * BQ;
-    const char* qt = q_s + buf * QTILE;
-    const char* dt_s = do_s + buf * QTILE;
+    const char* qt = smem + buf * 2 * QTILE;
+    const char* ot = qt + QTILE;
     const float* lt = lse_s + buf * BQ;
     const float* dl = dd_s + buf * BQ;
-    const bool edge = (k0 + wave * 32 + 32 > N) || (p.causal && k0 + wave * 32 + 31 > q0);
+    const bool edge = (kw0 + 32 > N) || (p.causal && kw0 + 31 > q0);
 
-    V8 pb[MQ][2], sb[MQ][2];
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
+      // S and dP for queries q0 + 32 mq + mrow (registers) x this lane's key
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        V8 a = as_v8<DT>(lds_read16(qt, tile_off<ROWB>(32 * mq + l32, 16 * c + 8 * g)));
-        s = DT::mma(a, kf[c], s);
-        V8 b = as_v8<DT>(lds_read16(dt_s, tile_off<ROWB>(32 * mq + l32, 16 * c + 8 * g)));
-        dp = DT::mma(b, vf[c], dp);
+        s = DT::mma(as_v8<DT>(lds_read16(qt, qoff[c] + 32 * mq * ROWB)), kf[c], s);
+        dp = DT::mma(as_v8<DT>(lds_read16(ot, qoff[c] + 32 * mq * ROWB)), vf[c], dp);
       }
       float pe[16], de[16];
 #pragma unroll
@@ -236,65 +252,61 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * jj + u;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[u]));
-          if (edge) {
-            const int q = q0 + 32 * mq + 8 * jj + 4 * g + u;
-            if (kw >= N || (p.causal && kw > q)) pv = 0.f;
-          }
-          pe[r] = pv;
-          de[r] = pv * (dp[r] - d4[u]);
+          pe[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[u]));
+          de[r] = dp[r] - d4[u];
         }
       }
-      pb[mq][0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
-      pb[mq][1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
-      sb[mq][0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
-      sb[mq][1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
-      // dS^T rows (keys) to LDS: queries 32 mq + 8 jj + 4 g + 0..3 are contiguous
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + 32 * mq + mrow(g, r);
+          if (kw >= N || (p.causal && kw > q)) pe[r] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) de[r] *= pe[r];
+      // B operands: slot i of half h <-> query 32 mq + 16 h + 8 (i / 4) + 4 g + i % 4
+      V8 pb[2], sb[2];
+      pb[0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+      pb[1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+      sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
+      sb[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+      // dS^T row (this lane's key) for dQ: each half of sb holds 4 consecutive queries
       {
         const int row = wave * 32 + l32;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          u32x2 w = pack4<DT>(de[4 * jj], de[4 * jj + 1], de[4 * jj + 2], de[4 * jj + 3]);
-          lds_write8(ds_s, tile_off<SROWB>(row, 32 * mq + 8 * jj + 4 * g), w);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = __builtin_bit_cast(u32x4, sb[h]);
+          const int qb0 = 32 * mq + 16 * h + 4 * g;
+          lds_write8(ds_s, tile_off<SROWB>(row, qb0), u32x2{w.x, w.y});
+          lds_write8(ds_s, tile_off<SROWB>(row, qb0 + 8), u32x2{w.z, w.w});
         }
       }
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's queries)
+      // dV^T += dO^T P and dK^T += Q^T dS (contraction over these 32 queries)
 #pragma unroll
-    for (int d0 = 0; d0 < D / 32; ++d0) {
+      for (int d0 = 0; d0 < DT32; ++d0) {
 #pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
-        const int mq = kc >> 1, h = kc & 1;
-        const int rb = 32 * mq + 16 * h + 4 * g;
-        V8 a = tr_operand<DT, ROWB, 8>(dt_s, rb, 32 * d0, lane);
-        dv[d0] = DT::mma(a, pb[mq][h], dv[d0]);
-        V8 b = tr_operand<DT, ROWB, 8>(qt, rb, 32 * d0, lane);
-        dk[d0] = DT::mma(b, sb[mq][h], dk[d0]);
+        for (int h = 0; h < 2; ++h) {
+          const int off = troff[d0] + (32 * mq + 16 * h) * ROWB;
+          dv[d0] = DT::mma(tr_pair<DT>(ot, off, 8 * ROWB), pb[h], dv[d0]);
+          dk[d0] = DT::mma(tr_pair<DT>(qt, off, 8 * ROWB), sb[h], dk[d0]);
+        }
       }
     }
 
     __syncthreads();   // dS^T of every wave is in LDS
 
-    // dQ tile: rows = queries, columns = head dims; contraction over the BK keys
+    // dQ tile(s): rows = queries, columns = head dims; contraction over the BK keys
 #pragma unroll
     for (int w = 0; w < DQ_PER_WAVE; ++w) {
-      const int tix = wave * DQ_PER_WAVE + w;
-      const int mq = tix / (D / 32), d0 = tix % (D / 32);
+      const int mq = dq_mq0 + w;
       f32x16 a = f32x16{};
 #pragma unroll
-      for (int kc = 0; kc < BK / 16; ++kc) {
-        const int rb = 16 * kc + 8 * g;
-        V8 x = tr_operand<DT, SROWB, 4>(ds_s, rb, 32 * mq, lane);     // dS[q][keys]
-        V8 y = tr_operand<DT, ROWB, 4>(k_s, rb, 32 * d0, lane);       // K[keys][dim]
-        a = DT::mma(x, y, a);
-      }
-      const int dim = 32 * d0 + l32;
+      for (int kc = 0; kc < BK / 16; ++kc)
+        a = DT::mma(tr_pair<DT>(ds_s, dsoff[w] + 16 * kc * SROWB, 8 * SROWB), ktf[kc], a);
+      const int vbase = ((q0 + 32 * mq + 4 * g) * D + 32 * dq_d0 + l32) * 4;   // rows >= N dropped
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * mq + mrow(g, r);
-        if (q < N) unsafeAtomicAdd(dq_g + (size_t)q * D + dim, a[r]);
-      }
+      for (int r = 0; r < 16; ++r) buf_atomic_add(dq_rs, vbase + (8 * (r >> 2) + (r & 3)) * D * 4, a[r]);
     }
 
     if (in < n_qt) sstore(buf ^ 1);
@@ -307,14 +319,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_kernel(BwdParams p) {
   if (kw < N) {
     T* __restrict__ dkg = reinterpret_cast<T*>(p.dk) + hoff + (size_t)kw * D;
     T* __restrict__ dvg = reinterpret_cast<T*>(p.dv) + hoff + (size_t)kw * D;
-    const float s = p.scale;
+    const float sc = p.scale;
 #pragma unroll
-    for (int d0 = 0; d0 < D / 32; ++d0)
+    for (int d0 = 0; d0 < DT32; ++d0)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int col = 32 * d0 + 8 * jj + 4 * g;
         *reinterpret_cast<u32x2*>(dkg + col) =
-            pack4<DT>(dk[d0][4 * jj] * s, dk[d0][4 * jj + 1] * s, dk[d0][4 * jj + 2] * s, dk[d0][4 * jj + 3] * s);
+            pack4<DT>(dk[d0][4 * jj] * sc, dk[d0][4 * jj + 1] * sc, dk[d0][4 * jj + 2] * sc, dk[d0][4 * jj + 3] * sc);
         *reinterpret_cast<u32x2*>(dvg + col) =
             pack4<DT>(dv[d0][4 * jj], dv[d0][4 * jj + 1], dv[d0][4 * jj + 2], dv[d0][4 * jj + 3]);
       }

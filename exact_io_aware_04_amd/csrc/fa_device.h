@@ -76,23 +76,23 @@ __device__ __forceinline__ u32x2 pack4(float a0, float a1, float a2, float a3) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of ROW_BYTES bytes, stored with a per-row XOR swizzle of the
-// 16-byte chunks so that 16 consecutive rows read at one column hit 16
-// distinct 16-byte bank groups (64 banks x 4 bytes).
+// LDS tiles: rows of ROW_BYTES (a multiple of 128) bytes whose 16-byte chunks
+// are permuted per row: chunk c of row r sits in slot c ^ h(r), with
+//   h(r) = 2 (r mod 4) + ((r / 4) mod 2).
+// LDS serves 128 bytes per clock from 32 four-byte banks, i.e. 8 slots of 16
+// bytes. The two access shapes used by the kernels are then conflict-free:
+//   * 8 lanes reading one chunk column of 8 consecutive rows (operand reads
+//     with ds_read_b128): h(r) mod 8 takes all 8 values;
+//   * 16 lanes of a transpose read covering 4 consecutive rows x 2 adjacent
+//     chunks: h(r) / 2 takes 4 distinct values, so chunk pairs never collide.
 // ---------------------------------------------------------------------------
-template <int ROW_BYTES>
-__device__ __forceinline__ int swz(int row) {
-  constexpr int CPR = ROW_BYTES / 16;
-  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row length");
-  if constexpr (CPR == 16) return row & 15;
-  else if constexpr (CPR == 8) return (row >> 1) & 7;
-  else return (row >> 2) & 3;
-}
-// Byte offset of element column `col` (16-bit elements) of row `row`.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Byte offset of 16-bit element column `col` of row `row`.
 template <int ROW_BYTES>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  int chunk = col >> 3;
-  return row * ROW_BYTES + ((chunk ^ swz<ROW_BYTES>(row)) << 4) + ((col & 7) << 1);
+  static_assert(ROW_BYTES % 128 == 0, "row length");
+  return row * ROW_BYTES + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
@@ -113,17 +113,74 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Operand with 8 contraction slots taken from rows {rb+0..3, rb+8..11} (or
-// {rb+0..3, rb+4..7} when STEP == 4) of a row-major LDS tile, at column
-// `colbase + (lane % 32)`. Rows are the contraction index, columns the free index.
-template <class DT, int ROW_BYTES, int STEP>
-__device__ __forceinline__ typename DT::V8 tr_operand(const char* tile, int rb, int colbase, int lane) {
+// Lane-dependent part of a transpose-read operand address: rows
+// rb + 4 (lane/32)... are supplied by the caller through `row0`; the lane adds
+// (lane % 16) / 4 to the row and reads columns colbase + (lane & 16) + 4 (lane % 4).
+template <int ROW_BYTES>
+__device__ __forceinline__ int tr_off(int row0, int colbase, int lane) {
   const int t = lane & 15;
-  const int col = colbase + (lane & 16) + 4 * (t & 3);
-  const int row = rb + (t >> 2);
-  u32x2 lo = lds_read_tr(tile + tile_off<ROW_BYTES>(row, col));
-  u32x2 hi = lds_read_tr(tile + tile_off<ROW_BYTES>(row + STEP, col));
+  return tile_off<ROW_BYTES>(row0 + (t >> 2), colbase + (lane & 16) + 4 * (t & 3));
+}
+
+// Operand with 8 contraction slots taken from two transpose reads at byte
+// offsets `off` and `off + step_bytes` (the second block of 4 rows).
+template <class DT>
+__device__ __forceinline__ typename DT::V8 tr_pair(const char* tile, int off, int step_bytes) {
+  u32x2 lo = lds_read_tr(tile + off);
+  u32x2 hi = lds_read_tr(tile + off + step_bytes);
   return as_v8<DT>(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: 128-bit descriptors (base, byte range) held in SGPRs.
+// Loads past the range return zero and atomics past it are dropped, which
+// takes care of ragged tails without per-element branches.
+// ---------------------------------------------------------------------------
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
+}
+
+// Sum of the 8 16-bit values of an operand register set, accumulated in fp32.
+template <class DT>
+__device__ __forceinline__ float sum8(typename DT::V8 v, float acc);
+template <>
+__device__ __forceinline__ float sum8<F16>(f16x8 v, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(_Float16)1.f, (_Float16)1.f};
+  acc = __builtin_amdgcn_fdot2(h2{v[0], v[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(h2{v[2], v[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(h2{v[4], v[5]}, one, acc, false);
+  return __builtin_amdgcn_fdot2(h2{v[6], v[7]}, one, acc, false);
+}
+template <>
+__device__ __forceinline__ float sum8<BF16>(bf16x8 v, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(__bf16)1.f, (__bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(b2{v[0], v[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(b2{v[2], v[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(b2{v[4], v[5]}, one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(b2{v[6], v[7]}, one, acc, false);
+}
+
+// Maximum / sum across the lane pair (l, l ^ 32) that shares one row.
+__device__ __forceinline__ float pair_max(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -137,9 +194,5 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
-__device__ __forceinline__ float wave_max_pair(float x) {
-  // lanes l and l ^ 32 hold the two halves of one row
-  return fmaxf(x, __shfl_xor(x, 32));
-}
 
 }  // namespace fa

@@ -41,6 +41,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   constexpr int PER_T = BN * CPR / NT;        // chunks per thread per tensor
   constexpr int KC = D / 16;                  // contraction chunks over d
   constexpr int NS = BN / 32;                 // 32-key sub-tiles per tile
+  constexpr int DT32 = D / 32;
   static_assert(PER_T * NT == BN * CPR, "tile copy split");
   static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
 
@@ -58,9 +59,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   const int qw = q0 + wave * 32 + l32;        // this lane's query row
 
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Qg = reinterpret_cast<const T*>(p.q) + hoff;
-  const T* __restrict__ Kg = reinterpret_cast<const T*>(p.k) + hoff;
-  const T* __restrict__ Vg = reinterpret_cast<const T*>(p.v) + hoff;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
 
   // ---- key-tile range and skipping
   const int n_tiles = (N + BN - 1) / BN;
@@ -73,41 +75,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
   auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
 
-  // ---- Q fragments (B operand): lane holds Q[qw][16c + 8g .. +7]
+  // ---- Q fragments (B operand of S^T): lane holds Q[qw][16c + 8g .. +7]; rows >= N read as zero
   V8 qf[KC];
-  {
-    const bool ok = qw < N;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qg + (size_t)(ok ? qw : 0) * D + 8 * g);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      u32x4 x = ok ? src[2 * c] : u32x4{0, 0, 0, 0};
-      qf[c] = as_v8<DT>(x);
-    }
+  for (int c = 0; c < KC; ++c) qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * D + 16 * c + 8 * g) * 2));
+
+  // ---- lane-constant LDS offsets
+  int koff[KC];                               // K operand: row l32, chunk 2c + g
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
+  int voff[DT32];                             // V^T operand: rows 4g + (lane%16)/4 (+ tile row base)
+#pragma unroll
+  for (int dt = 0; dt < DT32; ++dt) voff[dt] = tr_off<ROWB>(4 * g, 32 * dt, lane);
+  int goff[PER_T], soff[PER_T];               // tile copy: global byte offset in the tile, LDS offset
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {
+    const int idx = tid + u * NT;
+    const int r = idx / CPR, c = idx % CPR;
+    goff[u] = (r * D + 8 * c) * 2;
+    soff[u] = tile_off<ROWB>(r, 8 * c);
   }
 
-  f32x16 acc[D / 32];
+  f32x16 acc[DT32];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s (the reference point)
-  float l_run = 0.f;         // this lane's share of the row sum at m_run
+  for (int t = 0; t < DT32; ++t) acc[t] = f32x16{};
+  float m_run = -INFINITY;   // running reference point, in units of scale*log2(e)*s
+  float l_run = 0.f;         // this lane's share of the row sum relative to m_run
   const float c2 = p.scale_log2;
 
-  // ---- tile copy helpers
   u32x4 kr[PER_T], vr[PER_T];
   auto gload = [&](int j) {
-    const int k0 = j * BN;
+    // keys >= N read as zero; the tile base goes into the per-lane offset,
+    // which the range check covers
+    const int base = j * BN * D * 2;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int key = k0 + r;
-      if (key < N) {
-        kr[u] = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + c * 8);
-        vr[u] = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + c * 8);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
-      }
+      kr[u] = buf_load16(k_rs, goff[u] + base);
+      vr[u] = buf_load16(v_rs, goff[u] + base);
     }
   };
   auto sstore = [&](int buf) {
@@ -115,11 +119,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     char* vt = kt + TILE;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      const int idx = tid + u * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int off = tile_off<ROWB>(r, c * 8);
-      lds_write16(kt, off, kr[u]);
-      lds_write16(vt, off, vr[u]);
+      lds_write16(kt, soff[u], kr[u]);
+      lds_write16(vt, soff[u], vr[u]);
     }
   };
 
@@ -139,20 +140,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     const char* vt = kt + TILE;
     const int k0 = j * BN;
 
-    // S^T sub-tiles: rows = keys (k0 + 32 s + mrow), column = this lane's query
+    // S^T sub-tiles: rows = keys k0 + 32 t + mrow, column = this lane's query
     f32x16 s[NS];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       s[t] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        V8 a = as_v8<DT>(lds_read16(kt, tile_off<ROWB>(32 * t + l32, 16 * c + 8 * g)));
-        s[t] = DT::mma(a, qf[c], s[t]);
-      }
+      for (int c = 0; c < KC; ++c) s[t] = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s[t]);
     }
 
-    const bool edge = (k0 + BN > N) || (p.causal && k0 + BN - 1 > q0);
-    if (edge) {
+    if ((k0 + BN > N) || (p.causal && k0 + BN - 1 > q0)) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -162,47 +159,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
         }
     }
 
-    // row maximum over this tile (raw scores; the scale is positive)
+    // row maximum of this tile (raw scores; the scale is positive)
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < NS; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float m_tile = mx * c2;
+    const float m_tile = pair_max(mx) * c2;
     const bool need = m_tile > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
       if (need) m_run = m_tile;
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+      for (int t = 0; t < DT32; ++t) acc[t] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    // probabilities (relative to m_run), row-sum share, B operands of O^T += V^T P^T
+    // probabilities relative to m_use, packed as B operands of O^T += V^T P^T;
+    // the row-sum share adds exactly the rounded values the product uses
     V8 pb[NS][2];
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
       float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c2, -m_use));
-        l_run += e[r];
-      }
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c2, -m_use));
       pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+      l_run = sum8<DT>(pb[t][0], l_run);
+      l_run = sum8<DT>(pb[t][1], l_run);
     }
 
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < DT32; ++dt) {
 #pragma unroll
       for (int kc = 0; kc < BN / 16; ++kc) {
         const int t = kc >> 1, h = kc & 1;
-        V8 a = tr_operand<DT, ROWB, 8>(vt, 32 * t + 16 * h + 4 * g, 32 * dt, lane);
+        V8 a = tr_pair<DT>(vt, voff[dt] + (32 * t + 16 * h) * ROWB, 8 * ROWB);
         acc[dt] = DT::mma(a, pb[t][h], acc[dt]);
       }
     }
@@ -215,13 +208,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
 
   // ---- epilogue: O = O~ / l, LSE = m ln2 + ln l
   {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-    const float l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float l_tot = pair_sum(l_run);
     if (qw < N) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hoff + (size_t)qw * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < DT32; ++dt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           u32x2 w = pack4<DT>(acc[dt][4 * jj] * inv, acc[dt][4 * jj + 1] * inv,

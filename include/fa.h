@@ -53,7 +53,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,     /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,    /* B, H or N < 1, or B*H*N*d does not fit the 64-bit index range */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, N*d >= 2^29 (per-head offsets are 32-bit), or the grid is too large */
   FA_ERR_DTYPE = -3,    /* dt is not FA_F16 or FA_BF16 */
   FA_ERR_HEADDIM = -4,  /* d is not 64 or 128 */
   FA_ERR_MASK = -5,     /* block_mask given with mask_block != 128 */

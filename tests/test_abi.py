@@ -66,7 +66,7 @@ def bwd(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(lse=None), -1),
-    (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2), (dict(B=1 << 20, H=1 << 10, N=1 << 20), -2),
+    (dict(B=0), -2), (dict(H=-1), -2), (dict(N=0), -2), (dict(B=1 << 20, H=1 << 10, N=1 << 20), -2), (dict(N=1 << 22, d=128), -2), (dict(N=1 << 23), -2),
     (dict(dt=2), -3), (dict(dt=-1), -3),
     (dict(d=32), -4), (dict(d=96), -4), (dict(d=256), -4),
     (dict(block_mask=A, mask_block=64), -5),
