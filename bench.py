@@ -2,8 +2,7 @@
 """Throughput of the fused attention forward + backward on one MI355X.
 
 A step is one pass of the whole path over one batch: fa_fwd, then
-fa_bwd_preprocess and fa_bwd (which clears the dQ accumulator, runs the
-backward kernel and converts dQ). Inputs are drawn on the host, copied to HBM
+fa_bwd_preprocess and fa_bwd (the dQ kernel and the dK/dV kernel). Inputs are drawn on the host, copied to HBM
 before timing, and every output buffer is allocated once; the timed loop only
 enqueues the three C-ABI calls. Prints ONE JSON line on stdout.
 
@@ -146,7 +145,6 @@ def main() -> int:
     if w.backward:
         Dv = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(fa.fa_bwd_workspace_bytes(B, H, N, d) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
     bmp = bm.data_ptr() if bm is not None else None
@@ -162,7 +160,7 @@ def main() -> int:
 
     def bwd():
         return fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), Dv.data_ptr(),
-                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), B, H, N, d, dt, scale,
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, scale,
                          causal, bmp, 128, s)
 
     log(f"[bench] warmup {args.warmup}")

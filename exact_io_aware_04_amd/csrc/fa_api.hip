@@ -79,39 +79,28 @@ fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int 
                     "fa_bwd_preprocess");
 }
 
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if (check_shape(B, H, N, d) != FA_OK) return 0;
-  return (size_t)4 * (size_t)B * (size_t)H * (size_t)N * (size_t)d;
-}
-
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* D,
-                 void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, fa_dtype dt,
-                 float scale, int causal, const uint8_t* block_mask, int mask_block, void* stream) {
-  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
+                 const uint8_t* block_mask, int mask_block, void* stream) {
+  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv) return FA_ERR_NULL;
   FA_TRY(check_shape(B, H, N, d));
   FA_TRY(check_dtype(dt));
   FA_TRY(check_mask(block_mask, mask_block));
   FA_TRY(check_scale(scale));
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(D) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_ALIGN;
-
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const long long n = (long long)B * H * (long long)N * d;
-  float* acc = static_cast<float*>(workspace);
-  FA_TRY(hip_status(fa::launch_fill_zero(acc, n, st), "fa_bwd (clear workspace)"));
 
   fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.Dvec = D;
-  p.dq_acc = acc; p.dk = dk; p.dv = dv;
+  p.dq = dq; p.dk = dk; p.dv = dv;
   p.mask = block_mask;
   p.B = B; p.H = H; p.N = N; p.D = d;
   p.mask_tiles = (N + 127) / 128;
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  FA_TRY(hip_status(fa::launch_bwd(p, dt == FA_BF16, st), "fa_bwd"));
-  return hip_status(fa::launch_dq_convert(acc, dq, n, scale, dt == FA_BF16, st), "fa_bwd (dq convert)");
+  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_bwd");
 }
 
 const char* fa_status_string(fa_status s) {

@@ -1,25 +1,26 @@
 // Attention backward for gfx950: recompute P tile by tile from Q, K and the
-// saved log-sum-exp, and form dV, dK (on chip, per key block) and dQ (fp32
-// atomics into a workspace).
+// saved log-sum-exp and form dQ, dK, dV without atomics.
 //
 // Method: page 1 ("FlashAttention：不减少一次注意力计算，为什么反而更快"), key design 3:
 // P_ij is rebuilt from the saved row statistic, D_i = dO_i . O_i replaces the
-// row-wide reduction, dS = P o (dP - D), dV = P^T dO, dQ = dS K, dK = dS^T Q;
-// page 2 ("FlashAttention 入门"), backward section: dQ is accumulated across
-// blocks with atomic adds (so the backward is not bitwise deterministic).
+// row-wide reduction, dS = P o (dP - D), dV = P^T dO, dQ = dS K, dK = dS^T Q.
 // The softmax scale s enters S = s Q K^T, so dQ and dK carry a factor s.
+// Page 2 ("FlashAttention 入门", backward section) notes that the default
+// backward adds dQ across blocks with atomics and that a deterministic option
+// exists at some extra cost; on this chip device-scope fp32 atomics cost more
+// than recomputing S and dP once more, so this backward is the deterministic
+// form: two kernels, each owning its outputs.
 //
-// Work decomposition (one workgroup = NW waves = NW*32 keys of one head):
-//   * each wave keeps its 32 rows of K and V in VGPRs (B operands of
-//     S = Q K^T and dP = dO V^T) and its 32 x D fp32 dK^T / dV^T accumulators;
-//   * Q / dO tiles of BQ rows stream through LDS (double buffered);
-//   * S and dP are computed with queries on the accumulator's register index
-//     and keys on its lane index, so P and dS feed dV^T = dO^T P and
-//     dK^T = Q^T dS directly as B operands (contraction over queries), with
-//     dO^T / Q^T read from LDS by the transpose read;
-//   * dS^T of all NW waves goes to LDS; the waves then share the BQ x D dQ
-//     tile (contraction over the workgroup's keys) and add it to the fp32
-//     workspace with atomics.
+//   * dkdv_kernel: one workgroup = NW waves = NW*32 keys of one head. Each wave
+//     keeps its 32 rows of K and V in VGPRs (B operands of S = Q K^T and
+//     dP = dO V^T) and its fp32 dK^T / dV^T accumulators; Q / dO tiles stream
+//     through LDS (double buffered). S and dP keep queries on the accumulator's
+//     register index, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS directly
+//     as B operands, with dO^T / Q^T from LDS by the transpose read.
+//   * dq_kernel: one workgroup = NW waves = NW*32 queries, laid out like the
+//     forward: Q and dO fragments stay in VGPRs, K / V tiles stream through
+//     LDS, S^T and dP^T put one query per lane, and dS^T feeds
+//     dQ^T = K^T dS^T as a B operand with K^T from the transpose read.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -50,36 +51,14 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
   if (row < rows && c == 0) Dvec[row] = sum;
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, long long n) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i + 3 < n) {
-    *reinterpret_cast<f32x4*>(x + i) = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-    for (long long t = i; t < n; ++t) x[t] = 0.f;
-  }
-}
-
-template <class DT>
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, void* __restrict__ dq_,
-                                                         long long n, float scale) {
-  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-  typename DT::T* dq = reinterpret_cast<typename DT::T*>(dq_);
-  if (i + 3 < n) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(acc + i);
-    *reinterpret_cast<u32x2*>(dq + i) = pack4<DT>(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
-  } else {
-    for (long long t = i; t < n; ++t) dq[t] = (typename DT::T)(acc[t] * scale);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Main backward kernel
+// dK, dV: one workgroup per block of NW*32 keys, looping over query tiles
 // ---------------------------------------------------------------------------
 template <int D>
-struct BwdOccupancy { static constexpr int value = D <= 64 ? 2 : 1; };
+struct DkdvOccupancy { static constexpr int value = D <= 64 ? 2 : 1; };
 
 template <class DT, int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
   constexpr int NT = NW * 64;
@@ -87,28 +66,17 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
   constexpr int ROWB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int QTILE = BQ * ROWB;
-  constexpr int SROWB = BQ * 2;               // dS^T rows: keys, columns: queries
-  constexpr int STILE = BK * SROWB;
   constexpr int KC = D / 16;
   constexpr int MQ = BQ / 32;                 // 32-query halves per tile
   constexpr int DT32 = D / 32;
   constexpr int PER_T = BQ * CPR / NT;        // Q/dO chunks per thread
-  constexpr int KPER_T = BK * CPR / NT;
-  constexpr int DQ_TILES = MQ * DT32;
-  constexpr int DQ_PER_WAVE = DQ_TILES / NW;
-  static_assert(PER_T * NT == BQ * CPR && KPER_T * NT == BK * CPR, "copy split");
-  static_assert(DQ_PER_WAVE * NW == DQ_TILES && DQ_PER_WAVE >= 1, "dQ split");
-  static_assert(NW % DT32 == 0 || DT32 % NW == 0, "dQ tiles per wave share one head-dim block");
-  static_assert(BK == 128 && 128 % BQ == 0, "block-mask granularity");
-  static_assert(2 * QTILE >= BK * ROWB, "K staging fits the second Q/dO buffer pair");
+  static_assert(PER_T * NT == BQ * CPR, "copy split");
+  static_assert(128 % BK == 0 && 128 % BQ == 0, "block-mask granularity");
 
-  // [Q buf0 | dO buf0 | Q buf1 | dO buf1 | dS^T | lse2 x2 | D x2]; the K tile is
-  // staged once in the buf1 pair before the first Q/dO tile lands there.
-  __shared__ __attribute__((aligned(16))) char smem[4 * QTILE + STILE + 4 * BQ * 4];
-  char* const ds_s = smem + 4 * QTILE;
-  float* const lse_s = reinterpret_cast<float*>(ds_s + STILE);   // [2][BQ]
-  float* const dd_s = lse_s + 2 * BQ;                              // [2][BQ]
-  char* const k_s = smem + 2 * QTILE;
+  // [Q buf0 | dO buf0 | Q buf1 | dO buf1 | lse2 x2 | D x2]
+  __shared__ __attribute__((aligned(16))) char smem[4 * QTILE + 4 * BQ * 4];
+  float* const lse_s = reinterpret_cast<float*>(smem + 4 * QTILE);  // [2][BQ]
+  float* const dd_s = lse_s + 2 * BQ;                                // [2][BQ]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -127,7 +95,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
   const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
   const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
   const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
-  const auto dq_rs = make_rsrc(p.dq_acc + hoff, (uint32_t)N * D * 4);
   const float* __restrict__ lse_g = p.lse + (size_t)bh * N;
   const float* __restrict__ D_g = p.Dvec + (size_t)bh * N;
 
@@ -138,13 +105,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
     kf[c] = as_v8<DT>(buf_load16(k_rs, (kw * D + 16 * c + 8 * g) * 2));
     vf[c] = as_v8<DT>(buf_load16(v_rs, (kw * D + 16 * c + 8 * g) * 2));
   }
-  // ---- K tile to LDS, read back transposed as the B operand of dQ = dS K
-#pragma unroll
-  for (int u = 0; u < KPER_T; ++u) {
-    const int idx = tid + u * NT;
-    const int r = idx / CPR, c = idx % CPR;
-    lds_write16(k_s, tile_off<ROWB>(r, 8 * c), buf_load16(k_rs, ((k0 + r) * D + 8 * c) * 2));
-  }
 
   // ---- lane-constant LDS offsets
   int qoff[KC];                               // Q / dO operand rows l32, chunk 2c + g
@@ -153,13 +113,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
   int troff[DT32];                            // dO^T / Q^T operands: rows 4g + (lane%16)/4 (+ block base)
 #pragma unroll
   for (int d0 = 0; d0 < DT32; ++d0) troff[d0] = tr_off<ROWB>(4 * g, 32 * d0, lane);
-  // dQ work of this wave: head-dim block dq_d0, query halves dq_mq0 .. dq_mq0 + DQ_PER_WAVE - 1
-  const int dq_d0 = wave % DT32;
-  const int dq_mq0 = (wave / DT32) * DQ_PER_WAVE;
-  // (a column shift is not additive under the row swizzle, so one offset per tile)
-  int dsoff[DQ_PER_WAVE];
-#pragma unroll
-  for (int w = 0; w < DQ_PER_WAVE; ++w) dsoff[w] = tr_off<SROWB>(4 * g, 32 * (dq_mq0 + w), lane);
 
   // ---- query-tile range and skipping
   const int n_qt = (N + BQ - 1) / BQ;
@@ -217,12 +170,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
     sstore(0);
   }
   __syncthreads();
-  V8 ktf[BK / 16];                            // K[keys of chunk kc][dim 32 dq_d0 + l32]
-  {
-    const int koff = tr_off<ROWB>(4 * g, 32 * dq_d0, lane);
-#pragma unroll
-    for (int kc = 0; kc < BK / 16; ++kc) ktf[kc] = tr_pair<DT>(k_s, koff + 16 * kc * ROWB, 8 * ROWB);
-  }
   int buf = 0;
 
   while (i < n_qt) {
@@ -271,17 +218,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
       pb[1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
       sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
       sb[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
-      // dS^T row (this lane's key) for dQ: each half of sb holds 4 consecutive queries
-      {
-        const int row = wave * 32 + l32;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 w = __builtin_bit_cast(u32x4, sb[h]);
-          const int qb0 = 32 * mq + 16 * h + 4 * g;
-          lds_write8(ds_s, tile_off<SROWB>(row, qb0), u32x2{w.x, w.y});
-          lds_write8(ds_s, tile_off<SROWB>(row, qb0 + 8), u32x2{w.z, w.w});
-        }
-      }
       // dV^T += dO^T P and dK^T += Q^T dS (contraction over these 32 queries)
 #pragma unroll
       for (int d0 = 0; d0 < DT32; ++d0) {
@@ -292,21 +228,6 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
           dk[d0] = DT::mma(tr_pair<DT>(qt, off, 8 * ROWB), sb[h], dk[d0]);
         }
       }
-    }
-
-    __syncthreads();   // dS^T of every wave is in LDS
-
-    // dQ tile(s): rows = queries, columns = head dims; contraction over the BK keys
-#pragma unroll
-    for (int w = 0; w < DQ_PER_WAVE; ++w) {
-      const int mq = dq_mq0 + w;
-      f32x16 a = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < BK / 16; ++kc)
-        a = DT::mma(tr_pair<DT>(ds_s, dsoff[w] + 16 * kc * SROWB, 8 * SROWB), ktf[kc], a);
-      const int vbase = ((q0 + 32 * mq + 4 * g) * D + 32 * dq_d0 + l32) * 4;   // rows >= N dropped
-#pragma unroll
-      for (int r = 0; r < 16; ++r) buf_atomic_add(dq_rs, vbase + (8 * (r >> 2) + (r & 3)) * D * 4, a[r]);
     }
 
     if (in < n_qt) sstore(buf ^ 1);
@@ -334,6 +255,175 @@ __global__ __launch_bounds__(NW * 64, BwdOccupancy<D>::value) void bwd_kernel(Bw
 }
 
 // ---------------------------------------------------------------------------
+// dQ: one workgroup per block of NW*32 queries, looping over key tiles
+// ---------------------------------------------------------------------------
+template <class DT, int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
+  using T = typename DT::T;
+  using V8 = typename DT::V8;
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  constexpr int ROWB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BN * ROWB;
+  constexpr int PER_T = BN * CPR / NT;
+  constexpr int KC = D / 16;
+  constexpr int NS = BN / 32;
+  constexpr int DT32 = D / 32;
+  static_assert(PER_T * NT == BN * CPR, "tile copy split");
+  static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int N = p.N;
+
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int bh = logical / p.q_blocks;
+  int qb = logical - bh * p.q_blocks;
+  if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
+  const int q0 = qb * BM;
+  const int qw = q0 + wave * 32 + l32;        // this lane's query
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
+  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
+
+  const int n_tiles = (N + BN - 1) / BN;
+  int j_end = n_tiles;
+  if (p.causal) {
+    const int last_q = min(q0 + BM, N) - 1;
+    j_end = min(n_tiles, last_q / BN + 1);
+  }
+  const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
+  auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
+  auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
+
+  // ---- per-query state: Q and dO fragments (B operands of S^T and dP^T), LSE, D
+  V8 qf[KC], of[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * D + 16 * c + 8 * g) * 2));
+    of[c] = as_v8<DT>(buf_load16(do_rs, (qw * D + 16 * c + 8 * g) * 2));
+  }
+  float lse2 = INFINITY, dq_d = 0.f;          // rows past N or without a visible key: P = 0
+  if (qw < N) {
+    const float l = p.lse[(size_t)bh * N + qw];
+    if (l != -INFINITY) lse2 = l * kLog2e;
+    dq_d = p.Dvec[(size_t)bh * N + qw];
+  }
+
+  int koff[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) koff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
+  int ktoff[DT32];                            // K^T operand: rows 4g + (lane%16)/4 (+ block base)
+#pragma unroll
+  for (int dt = 0; dt < DT32; ++dt) ktoff[dt] = tr_off<ROWB>(4 * g, 32 * dt, lane);
+  int goff[PER_T], soff[PER_T];
+#pragma unroll
+  for (int u = 0; u < PER_T; ++u) {
+    const int idx = tid + u * NT;
+    const int r = idx / CPR, c = idx % CPR;
+    goff[u] = (r * D + 8 * c) * 2;
+    soff[u] = tile_off<ROWB>(r, 8 * c);
+  }
+
+  f32x16 acc[DT32];
+#pragma unroll
+  for (int t = 0; t < DT32; ++t) acc[t] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  u32x4 kr[PER_T], vr[PER_T];
+  auto gload = [&](int j) {
+    const int base = j * BN * D * 2;          // keys >= N read as zero
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      kr[u] = buf_load16(k_rs, goff[u] + base);
+      vr[u] = buf_load16(v_rs, goff[u] + base);
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* kt = smem + buf * 2 * TILE;
+#pragma unroll
+    for (int u = 0; u < PER_T; ++u) {
+      lds_write16(kt, soff[u], kr[u]);
+      lds_write16(kt + TILE, soff[u], vr[u]);
+    }
+  };
+
+  int j = next_kept(0);
+  if (j < j_end) {
+    gload(j);
+    sstore(0);
+  }
+  __syncthreads();
+  int buf = 0;
+
+  while (j < j_end) {
+    const int jn = next_kept(j + 1);
+    if (jn < j_end) gload(jn);
+    const char* kt = smem + buf * 2 * TILE;
+    const char* vt = kt + TILE;
+    const int k0 = j * BN;
+    const bool edge = (k0 + BN > N) || (p.causal && k0 + BN - 1 > q0);
+
+#pragma unroll
+    for (int t = 0; t < NS; ++t) {
+      // S^T and dP^T: rows = keys k0 + 32 t + mrow, column = this lane's query
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        s = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s);
+        dp = DT::mma(as_v8<DT>(lds_read16(vt, koff[c] + 32 * t * ROWB)), of[c], dp);
+      }
+      float de[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) de[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * t + mrow(g, r);
+          if (key >= N || (p.causal && key > qw)) de[r] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) de[r] *= dp[r] - dq_d;
+      V8 sb[2];
+      sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
+      sb[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+      // dQ^T += K^T dS^T over these 32 keys
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[dt] = DT::mma(tr_pair<DT>(kt, ktoff[dt] + (32 * t + 16 * h) * ROWB, 8 * ROWB), sb[h], acc[dt]);
+      }
+    }
+
+    if (jn < j_end) sstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    j = jn;
+  }
+
+  // ---- epilogue: lane holds query qw, dims 32 dt + mrow(g, r)
+  if (qw < N) {
+    T* __restrict__ dqg = reinterpret_cast<T*>(p.dq) + hoff + (size_t)qw * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<u32x2*>(dqg + 32 * dt + 8 * jj + 4 * g) =
+            pack4<DT>(acc[dt][4 * jj] * sc, acc[dt][4 * jj + 1] * sc, acc[dt][4 * jj + 2] * sc, acc[dt][4 * jj + 3] * sc);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* Dvec, long long rows, int D,
@@ -350,35 +440,26 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* Dvec, lon
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(float* x, long long n, hipStream_t st) {
-  const unsigned blocks = (unsigned)((n + 1023) / 1024);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, x, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_dq_convert(const float* acc, void* dq, long long n, float scale, int is_bf16,
-                             hipStream_t st) {
-  const unsigned blocks = (unsigned)((n + 1023) / 1024);
-  if (is_bf16) hipLaunchKernelGGL((dq_convert_kernel<BF16>), dim3(blocks), dim3(256), 0, st, acc, dq, n, scale);
-  else hipLaunchKernelGGL((dq_convert_kernel<F16>), dim3(blocks), dim3(256), 0, st, acc, dq, n, scale);
-  return hipGetLastError();
-}
-
-template <class DT, int D, int BQ, int NW>
+template <class DT, int D, int BQ, int NW, int BN_DQ>
 static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
   BwdParams p = p0;
-  constexpr int BK = NW * 32;
-  p.k_blocks = (p.N + BK - 1) / BK;
+  constexpr int BM = NW * 32;
+  p.q_blocks = (p.N + BM - 1) / BM;
+  p.k_blocks = (p.N + BM - 1) / BM;
+  p.total_blocks = p.B * p.H * p.q_blocks;
+  hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   p.total_blocks = p.B * p.H * p.k_blocks;
-  hipLaunchKernelGGL((bwd_kernel<DT, D, BQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  hipLaunchKernelGGL((dkdv_kernel<DT, D, BQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_bwd_t<BF16, 64, 64, 4>(p, st) : launch_bwd_t<F16, 64, 64, 4>(p, st);
+    return is_bf16 ? launch_bwd_t<BF16, 64, 64, 4, 128>(p, st) : launch_bwd_t<F16, 64, 64, 4, 128>(p, st);
   }
-  return is_bf16 ? launch_bwd_t<BF16, 128, 64, 4>(p, st) : launch_bwd_t<F16, 128, 64, 4>(p, st);
+  return is_bf16 ? launch_bwd_t<BF16, 128, 64, 4, 64>(p, st) : launch_bwd_t<F16, 128, 64, 4, 64>(p, st);
 }
 
 }  // namespace fa

@@ -28,7 +28,7 @@ struct BwdParams {
   const void* dO;
   const float* lse;
   const float* Dvec;
-  float* dq_acc;         // fp32 [B,H,N,D], zeroed before the main kernel
+  void* dq;
   void* dk;
   void* dv;
   const uint8_t* mask;
@@ -37,6 +37,7 @@ struct BwdParams {
   int causal;
   float scale;
   float scale_log2;
+  int q_blocks;          // set by the launcher
   int k_blocks;          // set by the launcher
   int total_blocks;      // set by the launcher
 };
@@ -44,9 +45,6 @@ struct BwdParams {
 hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* Dvec, long long rows, int D,
                                  int is_bf16, hipStream_t st);
-hipError_t launch_fill_zero(float* x, long long n, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st);
-hipError_t launch_dq_convert(const float* acc, void* dq, long long n, float scale, int is_bf16,
-                             hipStream_t st);
 
 }  // namespace fa

@@ -6,7 +6,7 @@ stream. There is no fallback: if the shared library is missing or fails to
 load, importing this module raises.
 
 The low-level functions keep the C names (`fa_fwd`, `fa_bwd_preprocess`,
-`fa_bwd`, `fa_bwd_workspace_bytes`, `fa_status_string`) and take integer
+`fa_bwd`, `fa_status_string`) and take integer
 device addresses. `forward` / `backward` are thin conveniences over torch
 tensors that allocate the outputs and call the same entry points.
 """
@@ -27,7 +27,7 @@ STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE",
 }
-EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_status_string")
 
 
 def _load() -> ctypes.CDLL:
@@ -41,15 +41,13 @@ def _load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
             "or python exact_io_aware_04_amd/build.py). There is no non-HIP fallback.")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.restype = i
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
-    lib.fa_bwd_workspace_bytes.restype = sz
-    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd.restype = i
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i]
     return lib
@@ -75,14 +73,10 @@ def fa_bwd_preprocess(o, dO, D, B, H, N, d, dt, stream) -> int:
     return _lib.fa_bwd_preprocess(o, dO, D, B, H, N, d, dt, stream)
 
 
-def fa_bwd_workspace_bytes(B, H, N, d) -> int:
-    return _lib.fa_bwd_workspace_bytes(B, H, N, d)
-
-
-def fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B, H, N, d, dt, scale, causal, block_mask,
-           mask_block, stream) -> int:
-    return _lib.fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, workspace, B, H, N, d, dt, scale, causal,
-                       block_mask, mask_block, stream)
+def fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask, mask_block,
+           stream) -> int:
+    return _lib.fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask,
+                       mask_block, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -147,7 +141,7 @@ def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, block_
 
 
 def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = False, block_mask=None,
-             mask_block: int = 128, workspace=None, D=None, stream=None):
+             mask_block: int = 128, D=None, stream=None):
     """Run fa_bwd_preprocess then fa_bwd; returns (dq, dk, dv, D)."""
     torch = _torch()
     B, H, N, d = _shape(q)
@@ -158,12 +152,9 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
     if D is None:
         D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), B, H, N, d, dt, s), "fa_bwd_preprocess")
-    if workspace is None:
-        nbytes = fa_bwd_workspace_bytes(B, H, N, d)
-        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, N, d, dt,
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
                 float(scale), int(bool(causal)), _ptr(block_mask), mask_block, s)
     _check(st, "fa_bwd")
     return dq, dk, dv, D

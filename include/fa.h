@@ -10,8 +10,8 @@
  *        (block-sparse variant: zero blocks skipped, exact inside kept blocks).
  *   [P2] "FlashAttention 入门：从 FA1 到 FA4 的 IO 感知注意力" (oripoin.cn),
  *        FA1 section (causal: keys j > i skipped or masked), backward section
- *        (dQ accumulated with atomic adds; the default backward is not bitwise
- *        deterministic while the forward is).
+ *        (the default backward adds dQ with atomics and is not bitwise
+ *        deterministic; a deterministic option exists).
  *   [P3] "FlashAttention" (lyirs.cc), forward-process section (unnormalised
  *        accumulator, one final division by l).
  *
@@ -76,20 +76,17 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D,
                             int B, int H, int N, int d, fa_dtype dt, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: 4*B*H*N*d (the float32 dQ accumulator).
- * Returns 0 for invalid shapes. */
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
-
 /* Backward by recomputation [P1 key design 3; P2 backward section].
  * Inputs: q, k, v, dO (the gradient of o), lse from fa_fwd and D from
  * fa_bwd_preprocess, with the same shape, scale, causal flag and mask as the
- * forward. Writes dq, dk, dv (dt, rounded to nearest even). `workspace`
- * (caller-owned, at least fa_bwd_workspace_bytes, 16-byte aligned) is cleared
- * and used as a float32 dQ accumulator. dq is summed with float32 atomic adds,
- * so its low bits may differ between runs; dk and dv are deterministic. */
+ * forward. Writes dq, dk, dv (dt, rounded to nearest even). P is rebuilt tile
+ * by tile from q, k and lse; no N x N buffer and no workspace is used. This is
+ * the deterministic form of the backward (no atomics): one kernel owns each
+ * key block's dk, dv rows, another each query block's dq rows, so identical
+ * inputs give identical bits. */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO,
                  const float* lse, const float* D, void* dq, void* dk, void* dv,
-                 void* workspace, int B, int H, int N, int d, fa_dtype dt, float scale,
+                 int B, int H, int N, int d, fa_dtype dt, float scale,
                  int causal, const uint8_t* block_mask, int mask_block, void* stream);
 
 /* Static, NUL-terminated description of a status code. */

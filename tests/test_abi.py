@@ -38,13 +38,6 @@ def test_status_strings():
     assert "unknown" in fa.fa_status_string(123)
 
 
-def test_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(2, 3, 100, 64) == 4 * 2 * 3 * 100 * 64
-    assert fa.fa_bwd_workspace_bytes(1, 8, 65536, 128) == 4 * 8 * 65536 * 128
-    assert fa.fa_bwd_workspace_bytes(0, 3, 100, 64) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 10, 96) == 0
-
-
 # Fake, never-dereferenced addresses: validation rejects before any HIP call.
 A = 1 << 20          # 16-byte aligned
 MIS = A + 8          # misaligned
@@ -58,7 +51,7 @@ def fwd(**kw):
 
 
 def bwd(**kw):
-    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, workspace=A, B=1, H=1, N=16, d=64,
+    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, B=1, H=1, N=16, d=64,
                 dt=fa.FA_F16, scale=0.125, causal=0, block_mask=None, mask_block=128, stream=None)
     args.update(kw)
     return fa.fa_bwd(*args.values())
@@ -78,10 +71,10 @@ def test_fwd_validation(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(workspace=None), -1), (dict(D=None), -1), (dict(dv=None), -1),
+    (dict(dq=None), -1), (dict(D=None), -1), (dict(dv=None), -1),
     (dict(N=0), -2), (dict(dt=7), -3), (dict(d=80), -4),
     (dict(block_mask=A, mask_block=256), -5),
-    (dict(workspace=MIS), -6), (dict(dq=MIS), -6),
+    (dict(dk=MIS), -6), (dict(dq=MIS), -6),
     (dict(scale=0.0), -8),
 ])
 def test_bwd_validation(kw, code):
