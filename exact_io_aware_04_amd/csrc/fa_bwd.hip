@@ -110,9 +110,12 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   int qoff[KC];                               // Q / dO operand rows l32, chunk 2c + g
 #pragma unroll
   for (int c = 0; c < KC; ++c) qoff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
-  int troff[DT32];                            // dO^T / Q^T operands: rows 4g + (lane%16)/4 (+ block base)
+  int troff[DT32][2];                         // dO^T / Q^T operands: rows 4g (+8) + (lane%16)/4 (+ block base)
 #pragma unroll
-  for (int d0 = 0; d0 < DT32; ++d0) troff[d0] = tr_off<ROWB>(4 * g, 32 * d0, lane);
+  for (int d0 = 0; d0 < DT32; ++d0) {
+    troff[d0][0] = tr_off<ROWB>(4 * g, 32 * d0, lane);
+    troff[d0][1] = tr_off<ROWB>(4 * g + 8, 32 * d0, lane);
+  }
 
   // ---- query-tile range and skipping
   const int n_qt = (N + BQ - 1) / BQ;
@@ -121,22 +124,20 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
   auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
 
-  int goff[PER_T], soff[PER_T];
-#pragma unroll
-  for (int u = 0; u < PER_T; ++u) {
-    const int idx = tid + u * NT;
-    const int r = idx / CPR, c = idx % CPR;
-    goff[u] = (r * D + 8 * c) * 2;
-    soff[u] = tile_off<ROWB>(r, 8 * c);
-  }
+  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
+  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
+  constexpr int RSTEP = NT / CPR;
+  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
+  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
+  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
   u32x4 qr[PER_T], dr[PER_T];
   float lse_r = 0.f, dd_r = 0.f;
   auto gload = [&](int i) {
     const int base = i * BQ * D * 2;          // rows >= N read as zero
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      qr[u] = buf_load16(q_rs, goff[u] + base);
-      dr[u] = buf_load16(do_rs, goff[u] + base);
+      qr[u] = buf_load16(q_rs, goff + u * RSTEP * D * 2 + base);
+      dr[u] = buf_load16(do_rs, goff + u * RSTEP * D * 2 + base);
     }
     if (tid < BQ) {
       const int q = i * BQ + tid;
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     char* qt = smem + buf * 2 * QTILE;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      lds_write16(qt, soff[u], qr[u]);
-      lds_write16(qt + QTILE, soff[u], dr[u]);
+      lds_write16(qt, soff + u * RSTEP * ROWB, qr[u]);
+      lds_write16(qt + QTILE, soff + u * RSTEP * ROWB, dr[u]);
     }
     if (tid < BQ) {
       lse_s[buf * BQ + tid] = lse_r;
@@ -223,9 +224,9 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
       for (int d0 = 0; d0 < DT32; ++d0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int off = troff[d0] + (32 * mq + 16 * h) * ROWB;
-          dv[d0] = DT::mma(tr_pair<DT>(ot, off, 8 * ROWB), pb[h], dv[d0]);
-          dk[d0] = DT::mma(tr_pair<DT>(qt, off, 8 * ROWB), sb[h], dk[d0]);
+          const int rb = (32 * mq + 16 * h) * ROWB;
+          dv[d0] = DT::mma(tr_pair<DT>(ot, troff[d0][0] + rb, troff[d0][1] + rb), pb[h], dv[d0]);
+          dk[d0] = DT::mma(tr_pair<DT>(qt, troff[d0][0] + rb, troff[d0][1] + rb), sb[h], dk[d0]);
         }
       }
     }
@@ -320,17 +321,18 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   int koff[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) koff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
-  int ktoff[DT32];                            // K^T operand: rows 4g + (lane%16)/4 (+ block base)
+  int ktoff[DT32][2];                         // K^T operand: rows 4g (+8) + (lane%16)/4 (+ block base)
 #pragma unroll
-  for (int dt = 0; dt < DT32; ++dt) ktoff[dt] = tr_off<ROWB>(4 * g, 32 * dt, lane);
-  int goff[PER_T], soff[PER_T];
-#pragma unroll
-  for (int u = 0; u < PER_T; ++u) {
-    const int idx = tid + u * NT;
-    const int r = idx / CPR, c = idx % CPR;
-    goff[u] = (r * D + 8 * c) * 2;
-    soff[u] = tile_off<ROWB>(r, 8 * c);
+  for (int dt = 0; dt < DT32; ++dt) {
+    ktoff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
+    ktoff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
+  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
+  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
+  constexpr int RSTEP = NT / CPR;
+  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
+  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
+  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
 
   f32x16 acc[DT32];
 #pragma unroll
@@ -342,16 +344,16 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     const int base = j * BN * D * 2;          // keys >= N read as zero
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      kr[u] = buf_load16(k_rs, goff[u] + base);
-      vr[u] = buf_load16(v_rs, goff[u] + base);
+      kr[u] = buf_load16(k_rs, goff + u * RSTEP * D * 2 + base);
+      vr[u] = buf_load16(v_rs, goff + u * RSTEP * D * 2 + base);
     }
   };
   auto sstore = [&](int buf) {
     char* kt = smem + buf * 2 * TILE;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      lds_write16(kt, soff[u], kr[u]);
-      lds_write16(kt + TILE, soff[u], vr[u]);
+      lds_write16(kt, soff + u * RSTEP * ROWB, kr[u]);
+      lds_write16(kt + TILE, soff + u * RSTEP * ROWB, vr[u]);
     }
   };
 
@@ -400,7 +402,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
       for (int dt = 0; dt < DT32; ++dt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          acc[dt] = DT::mma(tr_pair<DT>(kt, ktoff[dt] + (32 * t + 16 * h) * ROWB, 8 * ROWB), sb[h], acc[dt]);
+          acc[dt] = DT::mma(tr_pair<DT>(kt, ktoff[dt][0] + (32 * t + 16 * h) * ROWB,
+                                        ktoff[dt][1] + (32 * t + 16 * h) * ROWB), sb[h], acc[dt]);
       }
     }
 

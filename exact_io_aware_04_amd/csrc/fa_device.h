@@ -76,58 +76,69 @@ __device__ __forceinline__ u32x2 pack4(float a0, float a1, float a2, float a3) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of ROW_BYTES (a multiple of 128) bytes whose 16-byte chunks
-// are permuted per row: chunk c of row r sits in slot c ^ h(r), with
-//   h(r) = 2 (r mod 4) + ((r / 4) mod 2).
-// LDS serves 128 bytes per clock from 32 four-byte banks, i.e. 8 slots of 16
-// bytes. The two access shapes used by the kernels are then conflict-free:
-//   * 8 lanes reading one chunk column of 8 consecutive rows (operand reads
-//     with ds_read_b128): h(r) mod 8 takes all 8 values;
-//   * 16 lanes of a transpose read covering 4 consecutive rows x 2 adjacent
-//     chunks: h(r) / 2 takes 4 distinct values, so chunk pairs never collide.
+// LDS tiles: rows of ROW_BYTES (128 or 256) bytes whose 16-byte chunks are
+// permuted per row: chunk c of row r sits in slot c ^ h(r). gfx950 LDS serves
+// 256 bytes per clock from 64 four-byte banks, i.e. 16 slots of 16 bytes; the
+// permutation makes the two access shapes the kernels use conflict-free:
+//   * operand reads (ds_read_b128): 16 lanes read one chunk column of 16
+//     consecutive rows -> 16 distinct slots;
+//   * transpose reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows
+//     (aligned to 4) x 4 adjacent chunks (aligned to 4) -> 16 distinct slots.
+//   256-byte rows: h(r) = 4 (r mod 4) + (r / 4 mod 4)
+//   128-byte rows: h(r) = 4 (r / 2 mod 2) + (r / 4 mod 4)   (odd rows start at slot 8)
+// h repeats every 16 rows, so offsets of rows 16 apart differ by a constant.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(ROW_BYTES == 128 || ROW_BYTES == 256, "row length");
+  if constexpr (ROW_BYTES == 256) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 // Byte offset of 16-bit element column `col` of row `row`.
 template <int ROW_BYTES>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  static_assert(ROW_BYTES % 128 == 0, "row length");
-  return row * ROW_BYTES + (((col >> 3) ^ swz(row)) << 4) + ((col & 7) << 1);
+  return row * ROW_BYTES + (((col >> 3) ^ swz<ROW_BYTES>(row)) << 4) + ((col & 7) << 1);
 }
 
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
+  return *(const lds_u32x4*)((const __attribute__((address_space(3))) char*)(base) + off);
 }
 __device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
-  *reinterpret_cast<u32x4*>(base + off) = v;
+  *(lds_u32x4*)((__attribute__((address_space(3))) char*)(base) + off) = v;
 }
 __device__ __forceinline__ void lds_write8(char* base, int off, u32x2 v) {
-  *reinterpret_cast<u32x2*>(base + off) = v;
+  *(lds_u32x2*)((__attribute__((address_space(3))) char*)(base) + off) = v;
 }
 
 // gfx950 LDS transpose read. Within each group of 16 lanes, lane t supplies the
 // address of four consecutive 16-bit elements of row t/4 (columns 4*(t%4)..+3)
 // of a 4 x 16 block; lane t receives column t of that block (rows 0..3).
-__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+// The address is formed in the LDS address space so that constant parts of
+// the offset fold into the instruction's immediate field.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ const lds_char* to_lds(const char* p) { return (const lds_char*)(p); }
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(to_lds(base) + off));
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Lane-dependent part of a transpose-read operand address: rows
-// rb + 4 (lane/32)... are supplied by the caller through `row0`; the lane adds
-// (lane % 16) / 4 to the row and reads columns colbase + (lane & 16) + 4 (lane % 4).
+// Lane-dependent part of a transpose-read operand address. The lane reads
+// row row0 + (lane % 16) / 4 at columns colbase + (lane & 16) + 4 (lane % 4).
 template <int ROW_BYTES>
 __device__ __forceinline__ int tr_off(int row0, int colbase, int lane) {
   const int t = lane & 15;
   return tile_off<ROW_BYTES>(row0 + (t >> 2), colbase + (lane & 16) + 4 * (t & 3));
 }
 
-// Operand with 8 contraction slots taken from two transpose reads at byte
-// offsets `off` and `off + step_bytes` (the second block of 4 rows).
+// Operand with 8 contraction slots from two transpose reads (two blocks of 4
+// rows) at byte offsets off_lo and off_hi.
 template <class DT>
-__device__ __forceinline__ typename DT::V8 tr_pair(const char* tile, int off, int step_bytes) {
-  u32x2 lo = lds_read_tr(tile + off);
-  u32x2 hi = lds_read_tr(tile + off + step_bytes);
+__device__ __forceinline__ typename DT::V8 tr_pair(const char* tile, int off_lo, int off_hi) {
+  u32x2 lo = lds_read_tr(tile, off_lo);
+  u32x2 hi = lds_read_tr(tile, off_hi);
   return as_v8<DT>(lo, hi);
 }
 

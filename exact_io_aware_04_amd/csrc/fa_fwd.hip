@@ -84,17 +84,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   int koff[KC];                               // K operand: row l32, chunk 2c + g
 #pragma unroll
   for (int c = 0; c < KC; ++c) koff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
-  int voff[DT32];                             // V^T operand: rows 4g + (lane%16)/4 (+ tile row base)
+  int voff[DT32][2];                          // V^T operand: rows 4g (+8) + (lane%16)/4 (+ 16-row block base)
 #pragma unroll
-  for (int dt = 0; dt < DT32; ++dt) voff[dt] = tr_off<ROWB>(4 * g, 32 * dt, lane);
-  int goff[PER_T], soff[PER_T];               // tile copy: global byte offset in the tile, LDS offset
-#pragma unroll
-  for (int u = 0; u < PER_T; ++u) {
-    const int idx = tid + u * NT;
-    const int r = idx / CPR, c = idx % CPR;
-    goff[u] = (r * D + 8 * c) * 2;
-    soff[u] = tile_off<ROWB>(r, 8 * c);
+  for (int dt = 0; dt < DT32; ++dt) {
+    voff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
+    voff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
+  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
+  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
+  constexpr int RSTEP = NT / CPR;
+  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
+  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
+  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
 
   f32x16 acc[DT32];
 #pragma unroll
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     const int base = j * BN * D * 2;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      kr[u] = buf_load16(k_rs, goff[u] + base);
-      vr[u] = buf_load16(v_rs, goff[u] + base);
+      kr[u] = buf_load16(k_rs, goff + u * RSTEP * D * 2 + base);
+      vr[u] = buf_load16(v_rs, goff + u * RSTEP * D * 2 + base);
     }
   };
   auto sstore = [&](int buf) {
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     char* vt = kt + TILE;
 #pragma unroll
     for (int u = 0; u < PER_T; ++u) {
-      lds_write16(kt, soff[u], kr[u]);
-      lds_write16(vt, soff[u], vr[u]);
+      lds_write16(kt, soff + u * RSTEP * ROWB, kr[u]);
+      lds_write16(vt, soff + u * RSTEP * ROWB, vr[u]);
     }
   };
 
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < BN / 16; ++kc) {
         const int t = kc >> 1, h = kc & 1;
-        V8 a = tr_pair<DT>(vt, voff[dt] + (32 * t + 16 * h) * ROWB, 8 * ROWB);
+        const int rb = (32 * t + 16 * h) * ROWB;
+        V8 a = tr_pair<DT>(vt, voff[dt][0] + rb, voff[dt][1] + rb);
         acc[dt] = DT::mma(a, pb[t][h], acc[dt]);
       }
     }
