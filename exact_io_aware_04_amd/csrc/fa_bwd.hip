@@ -13,8 +13,8 @@
 //
 //   * dkdv_kernel: one workgroup = NW waves = NW*32 keys of one head. Each wave
 //     keeps its 32 rows of K and V in VGPRs (B operands of S = Q K^T and
-//     dP = dO V^T) and its fp32 dK^T / dV^T accumulators; Q / dO tiles stream
-//     through LDS (double buffered). S and dP keep queries on the accumulator's
+//     dP = dO V^T) and its fp32 dK^T / dV^T accumulators; Q / dO tiles are
+//     copied HBM -> LDS directly (double buffered). S and dP keep queries on the accumulator's
 //     register index, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS directly
 //     as B operands, with dO^T / Q^T from LDS by the transpose read.
 //   * dq_kernel: one workgroup = NW waves = NW*32 queries, laid out like the
@@ -69,8 +69,6 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   constexpr int KC = D / 16;
   constexpr int MQ = BQ / 32;                 // 32-query halves per tile
   constexpr int DT32 = D / 32;
-  constexpr int PER_T = BQ * CPR / NT;        // Q/dO chunks per thread
-  static_assert(PER_T * NT == BQ * CPR, "copy split");
   static_assert(128 % BK == 0 && 128 % BQ == 0, "block-mask granularity");
 
   // [Q buf0 | dO buf0 | Q buf1 | dO buf1 | lse2 x2 | D x2]
@@ -124,21 +122,14 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
   auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
 
-  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
-  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
-  constexpr int RSTEP = NT / CPR;
-  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
-  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
-  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
-  u32x4 qr[PER_T], dr[PER_T];
+  const TileCopy<ROWB, QTILE, NW> copy(wave, lane);
   float lse_r = 0.f, dd_r = 0.f;
-  auto gload = [&](int i) {
-    const int base = i * BQ * D * 2;          // rows >= N read as zero
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      qr[u] = buf_load16(q_rs, goff + u * RSTEP * D * 2 + base);
-      dr[u] = buf_load16(do_rs, goff + u * RSTEP * D * 2 + base);
-    }
+  // asynchronous copy of query tile i into LDS buffer buf (rows >= N arrive as
+  // zeros); its LSE / D go through registers and are stored by sstore()
+  auto gload = [&](int i, int buf) {
+    char* qt = smem + buf * 2 * QTILE;
+    copy.issue(q_rs, qt, i * BQ * D * 2);
+    copy.issue(do_rs, qt + QTILE, i * BQ * D * 2);
     if (tid < BQ) {
       const int q = i * BQ + tid;
       const float l = q < N ? lse_g[q] : -INFINITY;
@@ -148,12 +139,6 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     }
   };
   auto sstore = [&](int buf) {
-    char* qt = smem + buf * 2 * QTILE;
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      lds_write16(qt, soff + u * RSTEP * ROWB, qr[u]);
-      lds_write16(qt + QTILE, soff + u * RSTEP * ROWB, dr[u]);
-    }
     if (tid < BQ) {
       lse_s[buf * BQ + tid] = lse_r;
       dd_s[buf * BQ + tid] = dd_r;
@@ -167,15 +152,16 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   const float c2 = p.scale_log2;
   int i = next_kept(i_begin);
   if (i < n_qt) {
-    gload(i);
+    gload(i, 0);
     sstore(0);
   }
+  wait_tile_copies();
   __syncthreads();
   int buf = 0;
 
   while (i < n_qt) {
     const int in = next_kept(i + 1);
-    if (in < n_qt) gload(in);
+    if (in < n_qt) gload(in, buf ^ 1);       // that buffer was last read before the previous barrier
     const int q0 = i * BQ;
     const char* qt = smem + buf * 2 * QTILE;
     const char* ot = qt + QTILE;
@@ -232,6 +218,7 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     }
 
     if (in < n_qt) sstore(buf ^ 1);
+    wait_tile_copies();
     __syncthreads();
     buf ^= 1;
     i = in;
@@ -267,11 +254,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   constexpr int ROWB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int TILE = BN * ROWB;
-  constexpr int PER_T = BN * CPR / NT;
   constexpr int KC = D / 16;
   constexpr int NS = BN / 32;
   constexpr int DT32 = D / 32;
-  static_assert(PER_T * NT == BN * CPR, "tile copy split");
   static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
@@ -327,47 +312,29 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     ktoff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
     ktoff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
-  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
-  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
-  constexpr int RSTEP = NT / CPR;
-  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
-  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
-  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
+  const TileCopy<ROWB, TILE, NW> copy(wave, lane);
 
   f32x16 acc[DT32];
 #pragma unroll
   for (int t = 0; t < DT32; ++t) acc[t] = f32x16{};
   const float c2 = p.scale_log2;
 
-  u32x4 kr[PER_T], vr[PER_T];
-  auto gload = [&](int j) {
-    const int base = j * BN * D * 2;          // keys >= N read as zero
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      kr[u] = buf_load16(k_rs, goff + u * RSTEP * D * 2 + base);
-      vr[u] = buf_load16(v_rs, goff + u * RSTEP * D * 2 + base);
-    }
-  };
-  auto sstore = [&](int buf) {
+  // asynchronous copy of key tile j into LDS buffer buf (keys >= N arrive as zeros)
+  auto gload = [&](int j, int buf) {
     char* kt = smem + buf * 2 * TILE;
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      lds_write16(kt, soff + u * RSTEP * ROWB, kr[u]);
-      lds_write16(kt + TILE, soff + u * RSTEP * ROWB, vr[u]);
-    }
+    copy.issue(k_rs, kt, j * BN * D * 2);
+    copy.issue(v_rs, kt + TILE, j * BN * D * 2);
   };
 
   int j = next_kept(0);
-  if (j < j_end) {
-    gload(j);
-    sstore(0);
-  }
+  if (j < j_end) gload(j, 0);
+  wait_tile_copies();
   __syncthreads();
   int buf = 0;
 
   while (j < j_end) {
     const int jn = next_kept(j + 1);
-    if (jn < j_end) gload(jn);
+    if (jn < j_end) gload(jn, buf ^ 1);       // that buffer was last read before the previous barrier
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
     const int k0 = j * BN;
@@ -407,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
       }
     }
 
-    if (jn < j_end) sstore(buf ^ 1);
+    wait_tile_copies();
     __syncthreads();
     buf ^= 1;
     j = jn;

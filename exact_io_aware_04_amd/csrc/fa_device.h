@@ -162,6 +162,43 @@ __device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, int byt
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Asynchronous tile copy HBM -> LDS (buffer_load_dwordx4 ... lds). Each wave
+// instruction fills 1 KB of LDS: lane i's 16 bytes land at the wave's LDS
+// address + 16 i. A lane therefore fetches the global chunk that belongs at
+// its LDS slot under the row permutation; rows past the buffer range arrive as
+// zeros. The global tile is row-major with the same row length as the LDS
+// tile, and a wave's successive kilobytes are NW KB apart, a whole number of
+// swizzle periods, so one lane offset serves every chunk.
+// Completion is tracked by vmcnt: wait_tile_copies() before the barrier that
+// publishes the tile.
+// ---------------------------------------------------------------------------
+template <int ROW_BYTES, int TILE_BYTES, int NW>
+struct TileCopy {
+  static constexpr int PER_WAVE = TILE_BYTES / (1024 * NW);
+  static_assert(PER_WAVE * 1024 * NW == TILE_BYTES, "tile is a whole number of wave kilobytes");
+  static_assert(((1024 * NW) / ROW_BYTES) % 16 == 0, "successive kilobytes are whole swizzle periods apart");
+  int goff;    // lane's global byte offset inside the tile for its first kilobyte
+  int wave;    // wave index (uniform)
+  __device__ __forceinline__ TileCopy(int wave_, int lane) {
+    wave = __builtin_amdgcn_readfirstlane(wave_);
+    const int p = 1024 * wave + 16 * lane;
+    const int row = p / ROW_BYTES, slot = (p % ROW_BYTES) / 16;
+    goff = row * ROW_BYTES + ((slot ^ swz<ROW_BYTES>(row)) << 4);
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int gbase) const {
+#pragma unroll
+    for (int u = 0; u < PER_WAVE; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + 1024 * (wave + NW * u)), 16,
+          goff + gbase + u * NW * 1024, 0, 0, 0);
+  }
+};
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// tile copies above) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_tile_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Sum of the 8 16-bit values of an operand register set, accumulated in fp32.
 template <class DT>
 __device__ __forceinline__ float sum8(typename DT::V8 v, float acc);

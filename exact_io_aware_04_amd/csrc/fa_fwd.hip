@@ -11,8 +11,9 @@
 // Work decomposition (one workgroup = NW waves = NW*32 query rows of one head):
 //   * each wave owns 32 query rows; their Q fragments stay in VGPRs for the
 //     whole key loop (B operand of S^T = K Q^T, contraction over d);
-//   * K/V tiles of BN keys are copied HBM -> registers -> LDS (double buffered,
-//     the next tile's global loads are in flight while the current one is used);
+//   * K/V tiles of BN keys are copied HBM -> LDS directly (buffer loads with
+//     the LDS destination), double buffered: the next tile's copy is in
+//     flight while the current one is used;
 //   * S^T is computed so that each lane owns ONE query and 16 keys per 32-key
 //     sub-tile: the row max needs one cross-half exchange, and the
 //     probabilities P^T are already laid out as the B operand of
@@ -38,11 +39,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   constexpr int ROWB = D * 2;                 // bytes per K/V row
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = BN * ROWB;
-  constexpr int PER_T = BN * CPR / NT;        // chunks per thread per tensor
   constexpr int KC = D / 16;                  // contraction chunks over d
   constexpr int NS = BN / 32;                 // 32-key sub-tiles per tile
   constexpr int DT32 = D / 32;
-  static_assert(PER_T * NT == BN * CPR, "tile copy split");
   static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
 
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
@@ -90,12 +89,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     voff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
     voff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
-  // tile copy: thread tid moves chunk (tid % CPR) of rows tid / CPR + u * RSTEP;
-  // RSTEP is a multiple of the swizzle period, so LDS offsets step by a constant
-  constexpr int RSTEP = NT / CPR;
-  static_assert(RSTEP % 16 == 0, "copy rows step by whole swizzle periods");
-  const int goff = ((tid / CPR) * D + 8 * (tid % CPR)) * 2;
-  const int soff = tile_off<ROWB>(tid / CPR, 8 * (tid % CPR));
+  const TileCopy<ROWB, TILE, NW> copy(wave, lane);
 
   f32x16 acc[DT32];
 #pragma unroll
@@ -104,38 +98,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   float l_run = 0.f;         // this lane's share of the row sum relative to m_run
   const float c2 = p.scale_log2;
 
-  u32x4 kr[PER_T], vr[PER_T];
-  auto gload = [&](int j) {
-    // keys >= N read as zero; the tile base goes into the per-lane offset,
-    // which the range check covers
-    const int base = j * BN * D * 2;
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      kr[u] = buf_load16(k_rs, goff + u * RSTEP * D * 2 + base);
-      vr[u] = buf_load16(v_rs, goff + u * RSTEP * D * 2 + base);
-    }
-  };
-  auto sstore = [&](int buf) {
+  // asynchronous copy of key tile j into LDS buffer buf (keys >= N arrive as zeros)
+  auto gload = [&](int j, int buf) {
     char* kt = smem + buf * 2 * TILE;
-    char* vt = kt + TILE;
-#pragma unroll
-    for (int u = 0; u < PER_T; ++u) {
-      lds_write16(kt, soff + u * RSTEP * ROWB, kr[u]);
-      lds_write16(vt, soff + u * RSTEP * ROWB, vr[u]);
-    }
+    copy.issue(k_rs, kt, j * BN * D * 2);
+    copy.issue(v_rs, kt + TILE, j * BN * D * 2);
   };
 
   int j = next_kept(0);
-  if (j < j_end) {
-    gload(j);
-    sstore(0);
-  }
+  if (j < j_end) gload(j, 0);
+  wait_tile_copies();
   __syncthreads();
   int buf = 0;
 
   while (j < j_end) {
     const int jn = next_kept(j + 1);
-    if (jn < j_end) gload(jn);
+    if (jn < j_end) gload(jn, buf ^ 1);     // that buffer was last read before the previous barrier
 
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
@@ -202,7 +180,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
       }
     }
 
-    if (jn < j_end) sstore(buf ^ 1);
+    wait_tile_copies();
     __syncthreads();
     buf ^= 1;
     j = jn;
