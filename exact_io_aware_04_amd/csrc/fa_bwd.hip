@@ -13,8 +13,8 @@
 //
 //   * dkdv_kernel: one workgroup = NW waves = NW*32 keys of one head. Each wave
 //     keeps its 32 rows of K and V in VGPRs (B operands of S = Q K^T and
-//     dP = dO V^T) and its fp32 dK^T / dV^T accumulators; Q / dO tiles are
-//     copied HBM -> LDS directly (double buffered). S and dP keep queries on the accumulator's
+//     dP = dO V^T) and its fp32 dK^T / dV^T accumulators; Q / dO tiles of 128
+//     rows are copied HBM -> LDS directly (double buffered). S and dP keep queries on the accumulator's
 //     register index, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS directly
 //     as B operands, with dO^T / Q^T from LDS by the transpose read.
 //   * dq_kernel: one workgroup = NW waves = NW*32 queries, laid out like the
@@ -171,13 +171,30 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
 
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
+      // Q and dO rows of this 32-query half, read as one batch, then
       // S and dP for queries q0 + 32 mq + mrow (registers) x this lane's key
+      V8 qa[KC], oa[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        qa[c] = as_v8<DT>(lds_read16(qt, qoff[c] + 32 * mq * ROWB));
+        oa[c] = as_v8<DT>(lds_read16(ot, qoff[c] + 32 * mq * ROWB));
+      }
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        s = DT::mma(as_v8<DT>(lds_read16(qt, qoff[c] + 32 * mq * ROWB)), kf[c], s);
-        dp = DT::mma(as_v8<DT>(lds_read16(ot, qoff[c] + 32 * mq * ROWB)), vf[c], dp);
+        s = DT::mma(qa[c], kf[c], s);
+        dp = DT::mma(oa[c], vf[c], dp);
       }
+      // dO^T / Q^T operands of the dV / dK products, in flight while S and dP run
+      V8 ta[DT32][2], tb[DT32][2];
+#pragma unroll
+      for (int d0 = 0; d0 < DT32; ++d0)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rb = (32 * mq + 16 * h) * ROWB;
+          ta[d0][h] = tr_pair<DT>(ot, troff[d0][0] + rb, troff[d0][1] + rb);
+          tb[d0][h] = tr_pair<DT>(qt, troff[d0][0] + rb, troff[d0][1] + rb);
+        }
       float pe[16], de[16];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -210,9 +227,8 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
       for (int d0 = 0; d0 < DT32; ++d0) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int rb = (32 * mq + 16 * h) * ROWB;
-          dv[d0] = DT::mma(tr_pair<DT>(ot, troff[d0][0] + rb, troff[d0][1] + rb), pb[h], dv[d0]);
-          dk[d0] = DT::mma(tr_pair<DT>(qt, troff[d0][0] + rb, troff[d0][1] + rb), sb[h], dk[d0]);
+          dv[d0] = DT::mma(ta[d0][h], pb[h], dv[d0]);
+          dk[d0] = DT::mma(tb[d0][h], sb[h], dk[d0]);
         }
       }
     }
@@ -427,9 +443,9 @@ static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
 
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_bwd_t<BF16, 64, 64, 4, 128>(p, st) : launch_bwd_t<F16, 64, 64, 4, 128>(p, st);
+    return is_bf16 ? launch_bwd_t<BF16, 64, 128, 4, 128>(p, st) : launch_bwd_t<F16, 64, 128, 4, 128>(p, st);
   }
-  return is_bf16 ? launch_bwd_t<BF16, 128, 64, 4, 64>(p, st) : launch_bwd_t<F16, 128, 64, 4, 64>(p, st);
+  return is_bf16 ? launch_bwd_t<BF16, 128, 128, 4, 64>(p, st) : launch_bwd_t<F16, 128, 128, 4, 64>(p, st);
 }
 
 }  // namespace fa
