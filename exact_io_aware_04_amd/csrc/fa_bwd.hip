@@ -17,6 +17,8 @@
 //     rows are copied HBM -> LDS directly (double buffered). S and dP keep queries on the accumulator's
 //     register index, so P and dS feed dV^T = dO^T P and dK^T = Q^T dS directly
 //     as B operands, with dO^T / Q^T from LDS by the transpose read.
+//   * dkdv_split_kernel (d = 128): the same products split between wave pairs
+//     so that two waves per SIMD fit the register file (see below).
 //   * dq_kernel: one workgroup = NW waves = NW*32 queries, laid out like the
 //     forward: Q and dO fragments stay in VGPRs, K / V tiles stream through
 //     LDS, S^T and dP^T put one query per lane, and dS^T feeds
@@ -259,6 +261,272 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV for d = 128: role-split wave pairs, 8 waves (two per SIMD) and 128 keys
+// per workgroup. Waves w and w + 4 share the 32 keys of group w:
+//   role A (waves 0-3) keeps K and dV^T: S = Q K^T, P = exp2(S c - LSE) (rounded
+//     to the operand type, written to LDS), dV^T += dO^T P;
+//   role B (waves 4-7) keeps V and dK^T: dP = dO V^T, dS = P o (dP - D) with P
+//     read back from LDS, dK^T += Q^T dS.
+// B runs one query tile behind A: in step n, A forms dV of tile n and S, P of
+// tile n + 1 while B forms dS, dK of tile n and dP of tile n + 1, so one barrier
+// per tile suffices and each SIMD always has two waves with independent work.
+// Three Q/dO tile slots (tiles n and n + 1 in use, n + 2 arriving) and two P
+// buffers. dS uses the same rounded P that enters dV (an fp16/bf16 rounding of
+// P, inside the gradient tolerance).
+// ---------------------------------------------------------------------------
+template <class DT, int D, int BQ>
+__global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
+  using T = typename DT::T;
+  using V8 = typename DT::V8;
+  constexpr int NW = 8;
+  constexpr int BK = 128;                     // keys per workgroup
+  constexpr int ROWB = D * 2;
+  constexpr int QTILE = BQ * ROWB;
+  constexpr int KC = D / 16;
+  constexpr int MQ = BQ / 32;
+  constexpr int DT32 = D / 32;
+  constexpr int PBUF = 4 * MQ * 2 * 1024;     // P of one tile: [group][half][k][lane] x 16 bytes
+  static_assert(MQ == 2 && 128 % BQ == 0, "two 32-query halves per tile; block-mask granularity");
+
+  // [3 x (Q | dO)] [2 x P] [3 x lse2] [3 x D]
+  __shared__ __attribute__((aligned(16))) char smem[6 * QTILE + 2 * PBUF + 6 * BQ * 4];
+  char* const pbase = smem + 6 * QTILE;
+  float* const lse_s = reinterpret_cast<float*>(smem + 6 * QTILE + 2 * PBUF);
+  float* const dd_s = lse_s + 3 * BQ;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & 3;
+  const int N = p.N;
+
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int bh = logical / p.k_blocks;
+  const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
+  const int k0 = kb * BK;
+  const int kw0 = k0 + grp * 32;
+  const int kw = kw0 + l32;                   // this lane's key
+
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
+  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
+  const auto lse_rs = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const auto dvec_rs = make_rsrc(p.Dvec + (size_t)bh * N, (uint32_t)N * 4);
+
+  int qoff[KC];                               // operand rows l32, chunk 2c + g
+#pragma unroll
+  for (int c = 0; c < KC; ++c) qoff[c] = tile_off<ROWB>(l32, 16 * c + 8 * g);
+  int troff[DT32][2];                         // transposed operands: rows 4g (+8) + (lane%16)/4
+#pragma unroll
+  for (int d0 = 0; d0 < DT32; ++d0) {
+    troff[d0][0] = tr_off<ROWB>(4 * g, 32 * d0, lane);
+    troff[d0][1] = tr_off<ROWB>(4 * g + 8, 32 * d0, lane);
+  }
+
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int i_begin = p.causal ? k0 / BQ : 0;
+  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;
+  auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
+  auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
+
+  const TileCopy<ROWB, QTILE, NW> copy(wave, lane);
+  constexpr int PW = TileCopy<ROWB, QTILE, NW>::PER_WAVE;
+  // LSE / D of a tile go through registers: loaded before its tile copies are
+  // issued (so waiting for them never waits for the copies) and converted when
+  // stored into their slot
+  float lse_r = 0.f, dd_r = 0.f;
+  int i_ld = 0;
+  auto stat_load = [&](int i) {
+    i_ld = i;
+    if (tid < BQ) {
+      lse_r = buf_load_f32(lse_rs, (i * BQ + tid) * 4);
+      dd_r = buf_load_f32(dvec_rs, (i * BQ + tid) * 4);
+    }
+  };
+  auto stat_store = [&](int slot) {
+    if (tid < BQ) {
+      const int q = i_ld * BQ + tid;
+      // rows past N or with no visible key get P = exp2(s - inf) = 0
+      lse_s[slot * BQ + tid] = (q >= N || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
+      dd_s[slot * BQ + tid] = q < N ? dd_r : 0.f;
+    }
+  };
+
+  f32x16 acc[DT32];                           // A: dV^T, B: dK^T (lane: key kw, rows: dims)
+#pragma unroll
+  for (int t = 0; t < DT32; ++t) acc[t] = f32x16{};
+  const float c2 = p.scale_log2;
+
+  auto run = [&](auto role_tag) {
+    constexpr bool A = decltype(role_tag)::value;
+    V8 kvf[KC];                               // A: K rows, B: V rows (B operands, keys >= N read as zero)
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      kvf[c] = as_v8<DT>(buf_load16(A ? k_rs : v_rs, (kw * D + 16 * c + 8 * g) * 2));
+
+    V8 pb[MQ][2];                             // A: rounded P of the tile in flight
+    f32x16 dp[MQ];                            // B: dP of the tile in flight
+
+    // A: S and P of tile i (slot), P also to LDS buffer pslot; B: dP of tile i
+    auto front = [&](int i, int slot, int pslot) {
+      const char* qt = smem + slot * 2 * QTILE;
+      const char* ot = qt + QTILE;
+      const float* lt = lse_s + slot * BQ;
+      const int q0 = i * BQ;
+      const bool edge = (kw0 + 32 > N) || (p.causal && kw0 + 31 > q0);
+      char* pbuf = pbase + pslot * PBUF;
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        V8 xa[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) xa[c] = as_v8<DT>(lds_read16(A ? qt : ot, qoff[c] + 32 * mq * ROWB));
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) s = DT::mma(xa[c], kvf[c], s);
+        if constexpr (A) {
+          float pe[16];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 32 * mq + 8 * jj + 4 * g);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pe[4 * jj + u] = __builtin_amdgcn_exp2f(fmaf(s[4 * jj + u], c2, -l4[u]));
+          }
+          if (edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = q0 + 32 * mq + mrow(g, r);
+              if (kw >= N || (p.causal && kw > q)) pe[r] = 0.f;
+            }
+          }
+          pb[mq][0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+          pb[mq][1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            lds_write16(pbuf, (((grp * MQ + mq) * 2 + h) * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[mq][h]));
+        } else {
+          dp[mq] = s;
+        }
+      }
+    };
+
+    // A: dV^T += dO^T P; B: dS = P o (dP - D), dK^T += Q^T dS (tile in slot, P in pslot).
+    // Also issues this wave's share of the copy of tile il into slot lslot, one
+    // kilobyte every few products.
+    auto back = [&](int slot, int pslot, int il, int lslot) {
+      const char* qt = smem + slot * 2 * QTILE;
+      const char* ot = qt + QTILE;
+      const float* dl = dd_s + slot * BQ;
+      const char* pbuf = pbase + pslot * PBUF;
+      char* const nq = smem + lslot * 2 * QTILE;
+      constexpr int NMF = MQ * DT32 * 2;      // products in back()
+      static_assert(NMF % (2 * PW) == 0, "copy spread");
+      uint32_t ta[DT32][2];
+#pragma unroll
+      for (int d0 = 0; d0 < DT32; ++d0)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) ta[d0][k] = lds_addr(A ? ot : qt) + troff[d0][k];
+      static_for<0, MQ>([&](auto mqc) {
+        constexpr int mq = decltype(mqc)::value;
+        V8 tx[DT32][2];                       // A: dO^T, B: Q^T (rows 32 mq + 16 h ..)
+        static_for<0, 2>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+#pragma unroll
+          for (int d0 = 0; d0 < DT32; ++d0) tx[d0][h] = tr_pair_imm<DT, (32 * mq + 16 * h) * ROWB>(ta[d0][0], ta[d0][1]);
+        });
+        V8 bop[2];
+        if constexpr (A) {
+          bop[0] = pb[mq][0];
+          bop[1] = pb[mq][1];
+        } else {
+          float pe[16], de[16];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            unpack8<DT>(as_v8<DT>(lds_read16(pbuf, (((grp * MQ + mq) * 2 + h) * 64 + lane) * 16)), pe + 8 * h);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) de[4 * jj + u] = (dp[mq][4 * jj + u] - d4[u]) * pe[4 * jj + u];
+          }
+          bop[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
+          bop[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+        }
+#pragma unroll
+        for (int d0 = 0; d0 < DT32; ++d0) lds_wait_tie2(tx[d0][0], tx[d0][1]);
+#pragma unroll
+        for (int d0 = 0; d0 < DT32; ++d0)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int m = (mq * DT32 + d0) * 2 + h;
+            if (m % (NMF / (2 * PW)) == 0) {
+              const int u = m / (NMF / (2 * PW));
+              if (u < PW) copy.issue_one(q_rs, nq, il * BQ * D * 2, u);
+              else copy.issue_one(do_rs, nq + QTILE, il * BQ * D * 2, u - PW);
+            }
+            acc[d0] = DT::mma(tx[d0][h], bop[h], acc[d0]);
+          }
+      });
+    };
+
+    // prologue: the first two kept tiles resident, front() of the first
+    int i0 = next_kept(i_begin);
+    int i1 = i0 < n_qt ? next_kept(i0 + 1) : n_qt;
+    if (i0 < n_qt) {
+      stat_load(i0);
+      copy.issue(q_rs, smem, i0 * BQ * D * 2);
+      copy.issue(do_rs, smem + QTILE, i0 * BQ * D * 2);
+      stat_store(0);
+    }
+    if (i1 < n_qt) {
+      stat_load(i1);
+      copy.issue(q_rs, smem + 2 * QTILE, i1 * BQ * D * 2);
+      copy.issue(do_rs, smem + 3 * QTILE, i1 * BQ * D * 2);
+      stat_store(1);
+    }
+    wait_tile_copies();
+    __syncthreads();
+    if (i0 < n_qt) front(i0, 0, 0);
+    __syncthreads();
+    int n = 0;
+    while (i0 < n_qt) {
+      const int i2 = i1 < n_qt ? next_kept(i1 + 1) : n_qt;
+      const int s0 = n % 3, s1 = (n + 1) % 3, s2 = (n + 2) % 3;
+      // tile n + 2 into the idle slot s2 (past the last tile: this tile again, never read)
+      const int il = i2 < n_qt ? i2 : i0;
+      stat_load(il);
+      back(s0, n & 1, il, s2);
+      if (i1 < n_qt) front(i1, s1, (n + 1) & 1);
+      if (i2 < n_qt) stat_store(s2);
+      wait_tile_copies();
+      __syncthreads();
+      ++n;
+      i0 = i1;
+      i1 = i2;
+    }
+  };
+  if (wave < 4) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
+
+  // ---- epilogue: A writes dV, B writes dK = s dS^T Q (lane: key kw, dims 32 d0 + mrow)
+  if (kw < N) {
+    const bool isA = wave < 4;
+    T* __restrict__ dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hoff + (size_t)kw * D;
+    const float sc = isA ? 1.f : p.scale;
+#pragma unroll
+    for (int d0 = 0; d0 < DT32; ++d0)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = 32 * d0 + 8 * jj + 4 * g;
+        *reinterpret_cast<u32x2*>(dst + col) =
+            pack4<DT>(acc[d0][4 * jj] * sc, acc[d0][4 * jj + 1] * sc, acc[d0][4 * jj + 2] * sc, acc[d0][4 * jj + 3] * sc);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: one workgroup per block of NW*32 queries, looping over key tiles
 // ---------------------------------------------------------------------------
 template <class DT, int D, int BN, int NW>
@@ -426,26 +694,34 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* Dvec, lon
   return hipGetLastError();
 }
 
-template <class DT, int D, int BQ, int NW, int BN_DQ>
+// dq_kernel over 128-query blocks, then the dK/dV kernel over 128-key blocks:
+// dkdv_kernel (4 waves, 128-query tiles) at d = 64, dkdv_split_kernel (8 waves,
+// 64-query tiles) at d = 128.
+template <class DT, int D, int BN_DQ>
 static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
   BwdParams p = p0;
+  constexpr int NW = 4;
   constexpr int BM = NW * 32;
   p.q_blocks = (p.N + BM - 1) / BM;
-  p.k_blocks = (p.N + BM - 1) / BM;
+  p.k_blocks = (p.N + 127) / 128;
   p.total_blocks = p.B * p.H * p.q_blocks;
   hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.total_blocks = p.B * p.H * p.k_blocks;
-  hipLaunchKernelGGL((dkdv_kernel<DT, D, BQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((dkdv_kernel<DT, D, 128, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((dkdv_split_kernel<DT, D, 64>), dim3(p.total_blocks), dim3(512), 0, st, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_bwd_t<BF16, 64, 128, 4, 128>(p, st) : launch_bwd_t<F16, 64, 128, 4, 128>(p, st);
+    return is_bf16 ? launch_bwd_t<BF16, 64, 128>(p, st) : launch_bwd_t<F16, 64, 128>(p, st);
   }
-  return is_bf16 ? launch_bwd_t<BF16, 128, 128, 4, 64>(p, st) : launch_bwd_t<F16, 128, 128, 4, 64>(p, st);
+  return is_bf16 ? launch_bwd_t<BF16, 128, 64>(p, st) : launch_bwd_t<F16, 128, 64>(p, st);
 }
 
 }  // namespace fa

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -142,6 +144,41 @@ __device__ __forceinline__ typename DT::V8 tr_pair(const char* tile, int off_lo,
   return as_v8<DT>(lo, hi);
 }
 
+// The same transpose read issued as inline assembly with a compile-time byte
+// offset. The compiler makes every LDS access that it cannot prove disjoint
+// from an outstanding HBM -> LDS tile copy wait for all copies (the builtin
+// above is one); these reads are outside its view, so a copy into the other
+// buffer stays in flight. Their results are valid only after lds_wait_tie2().
+__device__ __forceinline__ uint32_t lds_addr(const char* p) { return (uint32_t)(size_t)to_lds(p); }
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_imm(uint32_t vaddr) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset field");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(vaddr), "n"(OFF));
+  return r;
+}
+template <class DT, int OFF>
+__device__ __forceinline__ typename DT::V8 tr_pair_imm(uint32_t a_lo, uint32_t a_hi) {
+  const u32x2 lo = tr_read_imm<OFF>(a_lo);
+  const u32x2 hi = tr_read_imm<OFF>(a_hi);
+  return as_v8<DT>(lo, hi);
+}
+// Wait for every outstanding LDS read of this wave; the operands are tied
+// through the wait so that no use of them is scheduled before it.
+template <class V>
+__device__ __forceinline__ void lds_wait_tie2(V& a, V& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Buffer resources: 128-bit descriptors (base, byte range) held in SGPRs.
 // Loads past the range return zero and atomics past it are dropped, which
@@ -186,6 +223,12 @@ struct TileCopy {
     const int row = p / ROW_BYTES, slot = (p % ROW_BYTES) / 16;
     goff = row * ROW_BYTES + ((slot ^ swz<ROW_BYTES>(row)) << 4);
   }
+  // kilobyte u (0 <= u < PER_WAVE) of this wave's share only
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, char* tile, int gbase, int u) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + 1024 * (wave + NW * u)), 16,
+        goff + gbase + u * NW * 1024, 0, 0, 0);
+  }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int gbase) const {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u)
@@ -198,6 +241,13 @@ struct TileCopy {
 // Wait until this wave's outstanding vector-memory operations (including the
 // tile copies above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_tile_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The 8 16-bit values of an operand register set, widened to fp32 (exact).
+template <class DT>
+__device__ __forceinline__ void unpack8(typename DT::V8 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+}
 
 // Sum of the 8 16-bit values of an operand register set, accumulated in fp32.
 template <class DT>
