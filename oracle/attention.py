@@ -24,7 +24,8 @@ design notes with its justification):
   * LSE is the natural log of the sum of exp of the *scaled* scores.
 
 All arrays are float64. One head is [N, d]; the batched helpers take
-[B, H, N, d] and loop over heads.
+[B, H, N, d] and loop over heads. Packed variable-length batches with grouped
+key/value heads are in oracle/varlen.py.
 """
 from __future__ import annotations
 
@@ -37,10 +38,15 @@ import numpy as np
 # Which (query, key) pairs take part
 # ---------------------------------------------------------------------------
 def kept_pairs(rows: np.ndarray, cols: np.ndarray, causal: bool,
-               block_mask: Optional[np.ndarray], mask_block: int) -> np.ndarray:
+               block_mask: Optional[np.ndarray], mask_block: int,
+               diag_offset: int = 0) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: True where key `col` is visible to query `row`.
 
-    causal: key j is visible to query i iff j <= i (square self-attention).
+    causal: key j is visible to query i iff j <= i + diag_offset. For square
+    self-attention diag_offset = 0; for n_q queries against n_k keys the
+    queries are read as the last n_q positions of the key sequence
+    (diag_offset = n_k - n_q, a reading: the pages only note that one backend
+    refuses causal attention with unequal lengths).
     block_mask: tile (i // mask_block, j // mask_block) must be nonzero.
     Both conditions combine with a logical AND.
     """
@@ -48,7 +54,7 @@ def kept_pairs(rows: np.ndarray, cols: np.ndarray, causal: bool,
     cols = np.asarray(cols, dtype=np.int64)
     keep = np.ones((rows.size, cols.size), dtype=bool)
     if causal:
-        keep &= cols[None, :] <= rows[:, None]
+        keep &= cols[None, :] <= rows[:, None] + diag_offset
     if block_mask is not None:
         bm = np.asarray(block_mask) != 0
         keep &= bm[(rows // mask_block)[:, None], (cols // mask_block)[None, :]]
@@ -83,12 +89,14 @@ def _probabilities(s):
 # ---------------------------------------------------------------------------
 def forward_head(q, k, v, scale: float, causal: bool = False,
                  block_mask: Optional[np.ndarray] = None, mask_block: int = 128,
-                 rows: Optional[Sequence[int]] = None, row_block: int = 1024):
+                 rows: Optional[Sequence[int]] = None, row_block: int = 1024,
+                 diag_offset: int = 0):
     """O = softmax(scale * q k^T) v and LSE for one head (or for selected rows).
 
-    q, k, v: [N, d] float64. Returns (O [R, d], LSE [R]) for the R requested
-    query rows (all rows by default). The score rows are materialised
-    `row_block` at a time only to bound host memory.
+    q: [N_q, d], k, v: [N_k, d] float64. Returns (O [R, d], LSE [R]) for the R
+    requested query rows (all rows by default). The score rows are
+    materialised `row_block` at a time only to bound host memory.
+    diag_offset: see kept_pairs (causal alignment for N_q != N_k).
     """
     n = k.shape[0]
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -97,7 +105,7 @@ def forward_head(q, k, v, scale: float, causal: bool = False,
     lse = np.empty(rows.size, dtype=np.float64)
     for r0 in range(0, rows.size, row_block):
         rr = rows[r0:r0 + row_block]
-        keep = kept_pairs(rr, cols, causal, block_mask, mask_block)
+        keep = kept_pairs(rr, cols, causal, block_mask, mask_block, diag_offset)
         p, lse[r0:r0 + rr.size] = _probabilities(_scores(q[rr], k, scale, keep))
         o[r0:r0 + rr.size] = p @ v
     return o, lse
@@ -105,7 +113,7 @@ def forward_head(q, k, v, scale: float, causal: bool = False,
 
 def backward_head(q, k, v, do, scale: float, causal: bool = False,
                   block_mask: Optional[np.ndarray] = None, mask_block: int = 128,
-                  row_block: int = 1024):
+                  row_block: int = 1024, diag_offset: int = 0):
     """Analytic gradients of O = softmax(scale q k^T) v for one head.
 
     With P the probabilities and dO the incoming gradient:
@@ -122,7 +130,7 @@ def backward_head(q, k, v, do, scale: float, causal: bool = False,
     dd = np.zeros(q.shape[0], dtype=np.float64)
     for r0 in range(0, q.shape[0], row_block):
         rr = np.arange(r0, min(r0 + row_block, q.shape[0]))
-        keep = kept_pairs(rr, cols, causal, block_mask, mask_block)
+        keep = kept_pairs(rr, cols, causal, block_mask, mask_block, diag_offset)
         p, _ = _probabilities(_scores(q[rr], k, scale, keep))
         dv += p.T @ do[rr]
         dp = do[rr] @ v.T
