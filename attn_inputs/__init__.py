@@ -171,3 +171,51 @@ def draw_workload(w: Workload, with_do: Optional[bool] = None) -> Drawn:
         with_do = w.backward
     return draw(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult, with_do)
 
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches (token-major [total, heads, d])
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class PackedDrawn:
+    """16-bit bit patterns of packed q [total_q, Hq, d], k and v [total_k, Hk, d],
+    do [total_q, Hq, d], and the cumulative offsets (int32, batch + 1)."""
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        return bits_to_f64(getattr(self, name), self.dtype)
+
+
+def cumulative(lengths) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def draw_packed(lengths_q, lengths_k, hq: int, hk: int, d: int, dtype: str, seed: int,
+                mult: float = 1.0) -> PackedDrawn:
+    """Draw packed q, k, v, do i.i.d. N(0,1) in fp32 from PCG64(seed), in that
+    order, multiply by `mult` and round to `dtype` (round-to-nearest-even)."""
+    cu_q, cu_k = cumulative(lengths_q), cumulative(lengths_k)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = [(int(cu_q[-1]), hq, d), (int(cu_k[-1]), hk, d), (int(cu_k[-1]), hk, d), (int(cu_q[-1]), hq, d)]
+    out = []
+    for shp in shapes:
+        x = rng.standard_normal(shp, dtype=np.float32)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        out.append(round_bits(x, dtype))
+    return PackedDrawn(dtype, out[0], out[1], out[2], out[3], cu_q, cu_k)
+
+
+def length_mix(batch: int, max_len: int, seed: int, min_len: int = 1) -> np.ndarray:
+    """Sequence lengths for a packed batch: uniform in [min_len, max_len] from
+    PCG64(seed), with the first entry pinned to max_len so the maximum is hit."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(min_len, max_len + 1, size=batch)
+    lens[0] = max_len
+    return lens.astype(np.int64)

@@ -38,6 +38,31 @@ fa_status check_scale(float s) { return (isfinite(s) && s > 0.f) ? FA_OK : FA_ER
 
 fa_status check_mask(const uint8_t* m, int mb) { return (m != nullptr && mb != 128) ? FA_ERR_MASK : FA_OK; }
 
+// Packed variable-length batches: byte offsets inside one (sequence, head) are
+// 32-bit (rows up to max_seqlen, heads x d elements apart), and the dispatch
+// grids (query blocks of 128 x 256 threads, key blocks of 128 x 512 threads)
+// count work-items in 32 bits.
+fa_status check_varlen(int batch, int total_q, int total_k, int max_q, int max_k, int Hq, int Hk, int d) {
+  if (batch < 1 || total_q < 0 || total_k < 0 || max_q < 1 || max_k < 1 || Hq < 1 || Hk < 1) return FA_ERR_SHAPE;
+  if (Hq % Hk != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((long long)max_q * Hq * d * 2 >= (1LL << 31) || (long long)max_k * Hk * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
+  if ((long long)max_q * Hq * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
+  const long double qg = (long double)batch * Hq * ((max_q + 127) / 128) * 256.0L;
+  const long double kg = (long double)batch * Hk * ((max_k + 127) / 128) * 512.0L;
+  if (qg > 4.0e9L || kg > 4.0e9L) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa::SeqLayout dense_layout(int H, int N) {
+  fa::SeqLayout L{};
+  L.cu_q = nullptr;
+  L.cu_k = nullptr;
+  L.Hk = H;
+  L.Nk = N;
+  return L;
+}
+
 #define FA_TRY(x)                     \
   do {                                \
     fa_status s_ = (x);               \
@@ -65,7 +90,34 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.mask_tiles = (N + 127) / 128;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.L = dense_layout(H, N);
   return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd");
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                        int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
+  FA_TRY(check_dtype(dt));
+  FA_TRY(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.mask = nullptr;
+  p.B = batch; p.H = Hq; p.N = max_seqlen_q; p.D = d;
+  p.mask_tiles = 0;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.L.cu_q = cu_seqlens_q;
+  p.L.cu_k = cu_seqlens_k;
+  p.L.total_q = total_q;
+  p.L.total_k = total_k;
+  p.L.Hk = Hk;
+  p.L.Nk = max_seqlen_k;
+  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_varlen");
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N, int d, fa_dtype dt,
@@ -100,14 +152,47 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, co
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.L = dense_layout(H, N);
   return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_bwd");
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                        const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                        int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                        void* stream) {
+  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_NULL;
+  FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
+  FA_TRY(check_dtype(dt));
+  FA_TRY(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) || !aligned16(D) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+
+  fa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.dO = dO; p.lse = lse; p.Dvec = D;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.mask = nullptr;
+  p.B = batch; p.H = Hq; p.N = max_seqlen_q; p.D = d;
+  p.mask_tiles = 0;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.L.cu_q = cu_seqlens_q;
+  p.L.cu_k = cu_seqlens_k;
+  p.L.total_q = total_q;
+  p.L.total_k = total_k;
+  p.L.Hk = Hk;
+  p.L.Nk = max_seqlen_k;
+  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_bwd_varlen");
 }
 
 const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H and N must be >= 1 and the tensor must fit the index range";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be >= 1 (heads: Hq a multiple of Hk) and fit the index range";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_F16 or FA_BF16";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
     case FA_ERR_MASK: return "FA_ERR_MASK: block_mask requires mask_block == 128";

@@ -83,27 +83,29 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, p.total_blocks);
-  const int bh = logical / p.k_blocks;
+  const int bh = logical / p.k_blocks;        // (sequence, key/value head)
   const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
   const int k0 = kb * BK;
   const int kw0 = k0 + wave * 32;
   const int kw = kw0 + l32;                   // this lane's key (column of S and dP)
+  const int b = bh / p.L.Hk, hk = bh - b * p.L.Hk;
+  const int grp = p.H / p.L.Hk;               // query heads reading this key/value head
+  const HeadView hv = head_view(p.L, b, hk * grp, p.H, N, D);
+  const int lq = hv.lq, lk = hv.lk;
+  if (k0 >= lk) return;                       // uniform: this block has no keys of its sequence
+  const int off = lk - lq;                    // causal: key j is seen by queries i >= j - off
 
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
-  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
-  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
-  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
-  const float* __restrict__ lse_g = p.lse + (size_t)bh * N;
-  const float* __restrict__ D_g = p.Dvec + (size_t)bh * N;
+  const uint32_t q_bytes = span_bytes(lq, hv.q_stride, D, 2), kv_bytes = span_bytes(lk, hv.kv_stride, D, 2);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hv.kv_off, kv_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hv.kv_off, kv_bytes);
+  const int q_rstride = hv.q_stride * 2;
 
-  // ---- K, V fragments (B operands of S = Q K^T and dP = dO V^T); keys >= N read as zero
+  // ---- K, V fragments (B operands of S = Q K^T and dP = dO V^T); keys past the sequence read as zero
   V8 kf[KC], vf[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    kf[c] = as_v8<DT>(buf_load16(k_rs, (kw * D + 16 * c + 8 * g) * 2));
-    vf[c] = as_v8<DT>(buf_load16(v_rs, (kw * D + 16 * c + 8 * g) * 2));
+    kf[c] = as_v8<DT>(buf_load16(k_rs, (kw * hv.kv_stride + 16 * c + 8 * g) * 2));
+    vf[c] = as_v8<DT>(buf_load16(v_rs, (kw * hv.kv_stride + 16 * c + 8 * g) * 2));
   }
 
   // ---- lane-constant LDS offsets
@@ -117,27 +119,36 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     troff[d0][1] = tr_off<ROWB>(4 * g + 8, 32 * d0, lane);
   }
 
-  // ---- query-tile range and skipping
-  const int n_qt = (N + BQ - 1) / BQ;
-  const int i_begin = p.causal ? k0 / BQ : 0;
-  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;
-  auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
-  auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
+  // ---- query tiles: every query head of the group x the tiles that see this key block.
+  // Flat index t -> head (t / nspan) of the group, tile i_begin + t % nspan.
+  const int n_qt = (lq + BQ - 1) / BQ;
+  const int i_begin = p.causal ? max(k0 - off, 0) / BQ : 0;
+  const int nspan = max(n_qt - i_begin, 0);
+  const int n_t = grp * nspan;
+  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;   // dense layout only
+  auto tile_i = [&](int t) { return i_begin + t % nspan; };
+  auto kept = [&](int t) {
+    return mcol == nullptr || mcol[(size_t)((tile_i(t) * BQ) / 128) * p.mask_tiles] != 0;
+  };
+  auto next_kept = [&](int t) { while (t < n_t && !kept(t)) ++t; return t; };
 
-  const TileCopy<ROWB, QTILE, NW> copy(wave, lane);
+  const TileCopy<ROWB, QTILE, NW> copy(wave, lane, q_rstride);
   float lse_r = 0.f, dd_r = 0.f;
-  // asynchronous copy of query tile i into LDS buffer buf (rows >= N arrive as
-  // zeros); its LSE / D go through registers and are stored by sstore()
-  auto gload = [&](int i, int buf) {
+  // asynchronous copy of flat tile t into LDS buffer buf (rows past the sequence
+  // arrive as zeros); its LSE / D go through registers and are stored by sstore()
+  auto gload = [&](int t, int buf) {
     char* qt = smem + buf * 2 * QTILE;
-    copy.issue(q_rs, qt, i * BQ * D * 2);
-    copy.issue(do_rs, qt + QTILE, i * BQ * D * 2);
+    const int hh = t / nspan, i = tile_i(t);
+    const size_t qo = hv.q_off + (size_t)hh * hv.q_hstep;
+    copy.issue(make_rsrc(reinterpret_cast<const T*>(p.q) + qo, q_bytes), qt, i * BQ * q_rstride);
+    copy.issue(make_rsrc(reinterpret_cast<const T*>(p.dO) + qo, q_bytes), qt + QTILE, i * BQ * q_rstride);
     if (tid < BQ) {
       const int q = i * BQ + tid;
-      const float l = q < N ? lse_g[q] : -INFINITY;
-      // rows past N or with no visible key get P = exp2(s - inf) = 0
+      const size_t si = hv.stat_off + (size_t)hh * hv.stat_hstep + (size_t)q * hv.stat_stride;
+      const float l = q < lq ? p.lse[si] : -INFINITY;
+      // rows past the sequence or with no visible key get P = exp2(s - inf) = 0
       lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dd_r = q < N ? D_g[q] : 0.f;
+      dd_r = q < lq ? p.Dvec[si] : 0.f;
     }
   };
   auto sstore = [&](int buf) {
@@ -152,24 +163,24 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   for (int t = 0; t < DT32; ++t) { dv[t] = f32x16{}; dk[t] = f32x16{}; }
 
   const float c2 = p.scale_log2;
-  int i = next_kept(i_begin);
-  if (i < n_qt) {
-    gload(i, 0);
+  int t = next_kept(0);
+  if (t < n_t) {
+    gload(t, 0);
     sstore(0);
   }
   wait_tile_copies();
   __syncthreads();
   int buf = 0;
 
-  while (i < n_qt) {
-    const int in = next_kept(i + 1);
-    if (in < n_qt) gload(in, buf ^ 1);       // that buffer was last read before the previous barrier
-    const int q0 = i * BQ;
+  while (t < n_t) {
+    const int tn = next_kept(t + 1);
+    if (tn < n_t) gload(tn, buf ^ 1);       // that buffer was last read before the previous barrier
+    const int q0 = tile_i(t) * BQ;
     const char* qt = smem + buf * 2 * QTILE;
     const char* ot = qt + QTILE;
     const float* lt = lse_s + buf * BQ;
     const float* dl = dd_s + buf * BQ;
-    const bool edge = (kw0 + 32 > N) || (p.causal && kw0 + 31 > q0);
+    const bool edge = (kw0 + 32 > lk) || (p.causal && kw0 + 31 > q0 + off);
 
 #pragma unroll
     for (int mq = 0; mq < MQ; ++mq) {
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = q0 + 32 * mq + mrow(g, r);
-          if (kw >= N || (p.causal && kw > q)) pe[r] = 0.f;
+          if (kw >= lk || (p.causal && kw > q + off)) pe[r] = 0.f;
         }
       }
 #pragma unroll
@@ -235,17 +246,17 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
       }
     }
 
-    if (in < n_qt) sstore(buf ^ 1);
+    if (tn < n_t) sstore(buf ^ 1);
     wait_tile_copies();
     __syncthreads();
     buf ^= 1;
-    i = in;
+    t = tn;
   }
 
   // ---- epilogue: lane holds key kw, dims 32 d0 + mrow(g, r)
-  if (kw < N) {
-    T* __restrict__ dkg = reinterpret_cast<T*>(p.dk) + hoff + (size_t)kw * D;
-    T* __restrict__ dvg = reinterpret_cast<T*>(p.dv) + hoff + (size_t)kw * D;
+  if (kw < lk) {
+    T* __restrict__ dkg = reinterpret_cast<T*>(p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
+    T* __restrict__ dvg = reinterpret_cast<T*>(p.dv) + hv.kv_off + (size_t)kw * hv.kv_stride;
     const float sc = p.scale;
 #pragma unroll
     for (int d0 = 0; d0 < DT32; ++d0)
@@ -301,20 +312,23 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, p.total_blocks);
-  const int bh = logical / p.k_blocks;
+  const int bh = logical / p.k_blocks;        // (sequence, key/value head)
   const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
   const int k0 = kb * BK;
   const int kw0 = k0 + grp * 32;
   const int kw = kw0 + l32;                   // this lane's key
+  const int b = bh / p.L.Hk, hk = bh - b * p.L.Hk;
+  const int qgrp = p.H / p.L.Hk;              // query heads reading this key/value head
+  const HeadView hv = head_view(p.L, b, hk * qgrp, p.H, N, D);
+  const int lq = hv.lq, lk = hv.lk;
+  if (k0 >= lk) return;                       // uniform: this block has no keys of its sequence
+  const int off = lk - lq;                    // causal: key j is seen by queries i >= j - off
 
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
-  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
-  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
-  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
-  const auto lse_rs = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4);
-  const auto dvec_rs = make_rsrc(p.Dvec + (size_t)bh * N, (uint32_t)N * 4);
+  const uint32_t q_bytes = span_bytes(lq, hv.q_stride, D, 2), kv_bytes = span_bytes(lk, hv.kv_stride, D, 2);
+  const uint32_t stat_bytes = span_bytes(lq, hv.stat_stride, 1, 4);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hv.kv_off, kv_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hv.kv_off, kv_bytes);
+  const int q_rstride = hv.q_stride * 2;
 
   int qoff[KC];                               // operand rows l32, chunk 2c + g
 #pragma unroll
@@ -326,32 +340,50 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
     troff[d0][1] = tr_off<ROWB>(4 * g + 8, 32 * d0, lane);
   }
 
-  const int n_qt = (N + BQ - 1) / BQ;
-  const int i_begin = p.causal ? k0 / BQ : 0;
-  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;
-  auto kept = [&](int i) { return mcol == nullptr || mcol[(size_t)((i * BQ) / 128) * p.mask_tiles] != 0; };
-  auto next_kept = [&](int i) { while (i < n_qt && !kept(i)) ++i; return i; };
+  // query tiles: every query head of the group x the tiles that see this key
+  // block; flat index t -> head t / nspan of the group, tile i_begin + t % nspan
+  const int n_qt = (lq + BQ - 1) / BQ;
+  const int i_begin = p.causal ? max(k0 - off, 0) / BQ : 0;
+  const int nspan = max(n_qt - i_begin, 0);
+  const int n_t = qgrp * nspan;
+  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;   // dense layout only
+  auto tile_i = [&](int t) { return i_begin + t % nspan; };
+  auto kept = [&](int t) {
+    return mcol == nullptr || mcol[(size_t)((tile_i(t) * BQ) / 128) * p.mask_tiles] != 0;
+  };
+  auto next_kept = [&](int t) { while (t < n_t && !kept(t)) ++t; return t; };
+  auto q_of = [&](int t) { return hv.q_off + (size_t)(t / nspan) * hv.q_hstep; };
+  auto stat_of = [&](int t) { return hv.stat_off + (size_t)(t / nspan) * hv.stat_hstep; };
 
-  const TileCopy<ROWB, QTILE, NW> copy(wave, lane);
+  const TileCopy<ROWB, QTILE, NW> copy(wave, lane, q_rstride);
   constexpr int PW = TileCopy<ROWB, QTILE, NW>::PER_WAVE;
   // LSE / D of a tile go through registers: loaded before its tile copies are
   // issued (so waiting for them never waits for the copies) and converted when
   // stored into their slot
   float lse_r = 0.f, dd_r = 0.f;
   int i_ld = 0;
-  auto stat_load = [&](int i) {
+  auto stat_load = [&](int t) {
+    const int i = tile_i(t);
     i_ld = i;
     if (tid < BQ) {
-      lse_r = buf_load_f32(lse_rs, (i * BQ + tid) * 4);
-      dd_r = buf_load_f32(dvec_rs, (i * BQ + tid) * 4);
+      const auto lse_rs = make_rsrc(p.lse + stat_of(t), stat_bytes);
+      const auto dvec_rs = make_rsrc(p.Dvec + stat_of(t), stat_bytes);
+      lse_r = buf_load_f32(lse_rs, (i * BQ + tid) * hv.stat_stride * 4);
+      dd_r = buf_load_f32(dvec_rs, (i * BQ + tid) * hv.stat_stride * 4);
     }
+  };
+  auto copy_tile = [&](int t, int slot) {
+    char* qt = smem + slot * 2 * QTILE;
+    const size_t qo = q_of(t);
+    copy.issue(make_rsrc(reinterpret_cast<const T*>(p.q) + qo, q_bytes), qt, tile_i(t) * BQ * q_rstride);
+    copy.issue(make_rsrc(reinterpret_cast<const T*>(p.dO) + qo, q_bytes), qt + QTILE, tile_i(t) * BQ * q_rstride);
   };
   auto stat_store = [&](int slot) {
     if (tid < BQ) {
       const int q = i_ld * BQ + tid;
       // rows past N or with no visible key get P = exp2(s - inf) = 0
-      lse_s[slot * BQ + tid] = (q >= N || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
-      dd_s[slot * BQ + tid] = q < N ? dd_r : 0.f;
+      lse_s[slot * BQ + tid] = (q >= lq || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
+      dd_s[slot * BQ + tid] = q < lq ? dd_r : 0.f;
     }
   };
 
@@ -365,18 +397,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
     V8 kvf[KC];                               // A: K rows, B: V rows (B operands, keys >= N read as zero)
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      kvf[c] = as_v8<DT>(buf_load16(A ? k_rs : v_rs, (kw * D + 16 * c + 8 * g) * 2));
+      kvf[c] = as_v8<DT>(buf_load16(A ? k_rs : v_rs, (kw * hv.kv_stride + 16 * c + 8 * g) * 2));
 
     V8 pb[MQ][2];                             // A: rounded P of the tile in flight
     f32x16 dp[MQ];                            // B: dP of the tile in flight
 
-    // A: S and P of tile i (slot), P also to LDS buffer pslot; B: dP of tile i
-    auto front = [&](int i, int slot, int pslot) {
+    // A: S and P of flat tile t (slot), P also to LDS buffer pslot; B: dP of tile t
+    auto front = [&](int t, int slot, int pslot) {
       const char* qt = smem + slot * 2 * QTILE;
       const char* ot = qt + QTILE;
       const float* lt = lse_s + slot * BQ;
-      const int q0 = i * BQ;
-      const bool edge = (kw0 + 32 > N) || (p.causal && kw0 + 31 > q0);
+      const int q0 = tile_i(t) * BQ;
+      const bool edge = (kw0 + 32 > lk) || (p.causal && kw0 + 31 > q0 + off);
       char* pbuf = pbase + pslot * PBUF;
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq) {
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int q = q0 + 32 * mq + mrow(g, r);
-              if (kw >= N || (p.causal && kw > q)) pe[r] = 0.f;
+              if (kw >= lk || (p.causal && kw > q + off)) pe[r] = 0.f;
             }
           }
           pb[mq][0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
@@ -413,14 +445,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
     };
 
     // A: dV^T += dO^T P; B: dS = P o (dP - D), dK^T += Q^T dS (tile in slot, P in pslot).
-    // Also issues this wave's share of the copy of tile il into slot lslot, one
-    // kilobyte every few products.
-    auto back = [&](int slot, int pslot, int il, int lslot) {
+    // Also issues this wave's share of the copy of flat tile tl into slot lslot,
+    // one kilobyte every few products.
+    auto back = [&](int slot, int pslot, int tl, int lslot) {
       const char* qt = smem + slot * 2 * QTILE;
       const char* ot = qt + QTILE;
       const float* dl = dd_s + slot * BQ;
       const char* pbuf = pbase + pslot * PBUF;
       char* const nq = smem + lslot * 2 * QTILE;
+      const size_t nqo = q_of(tl);
+      const auto nq_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + nqo, q_bytes);
+      const auto ndo_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + nqo, q_bytes);
+      const int ngb = tile_i(tl) * BQ * q_rstride;
       constexpr int NMF = MQ * DT32 * 2;      // products in back()
       static_assert(NMF % (2 * PW) == 0, "copy spread");
       uint32_t ta[DT32][2];
@@ -463,8 +499,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
             const int m = (mq * DT32 + d0) * 2 + h;
             if (m % (NMF / (2 * PW)) == 0) {
               const int u = m / (NMF / (2 * PW));
-              if (u < PW) copy.issue_one(q_rs, nq, il * BQ * D * 2, u);
-              else copy.issue_one(do_rs, nq + QTILE, il * BQ * D * 2, u - PW);
+              if (u < PW) copy.issue_one(nq_rs, nq, ngb, u);
+              else copy.issue_one(ndo_rs, nq + QTILE, ngb, u - PW);
             }
             acc[d0] = DT::mma(tx[d0][h], bop[h], acc[d0]);
           }
@@ -472,48 +508,46 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
     };
 
     // prologue: the first two kept tiles resident, front() of the first
-    int i0 = next_kept(i_begin);
-    int i1 = i0 < n_qt ? next_kept(i0 + 1) : n_qt;
-    if (i0 < n_qt) {
-      stat_load(i0);
-      copy.issue(q_rs, smem, i0 * BQ * D * 2);
-      copy.issue(do_rs, smem + QTILE, i0 * BQ * D * 2);
+    int t0 = next_kept(0);
+    int t1 = t0 < n_t ? next_kept(t0 + 1) : n_t;
+    if (t0 < n_t) {
+      stat_load(t0);
+      copy_tile(t0, 0);
       stat_store(0);
     }
-    if (i1 < n_qt) {
-      stat_load(i1);
-      copy.issue(q_rs, smem + 2 * QTILE, i1 * BQ * D * 2);
-      copy.issue(do_rs, smem + 3 * QTILE, i1 * BQ * D * 2);
+    if (t1 < n_t) {
+      stat_load(t1);
+      copy_tile(t1, 1);
       stat_store(1);
     }
     wait_tile_copies();
     __syncthreads();
-    if (i0 < n_qt) front(i0, 0, 0);
+    if (t0 < n_t) front(t0, 0, 0);
     __syncthreads();
     int n = 0;
-    while (i0 < n_qt) {
-      const int i2 = i1 < n_qt ? next_kept(i1 + 1) : n_qt;
+    while (t0 < n_t) {
+      const int t2 = t1 < n_t ? next_kept(t1 + 1) : n_t;
       const int s0 = n % 3, s1 = (n + 1) % 3, s2 = (n + 2) % 3;
       // tile n + 2 into the idle slot s2 (past the last tile: this tile again, never read)
-      const int il = i2 < n_qt ? i2 : i0;
-      stat_load(il);
-      back(s0, n & 1, il, s2);
-      if (i1 < n_qt) front(i1, s1, (n + 1) & 1);
-      if (i2 < n_qt) stat_store(s2);
+      const int tl = t2 < n_t ? t2 : t0;
+      stat_load(tl);
+      back(s0, n & 1, tl, s2);
+      if (t1 < n_t) front(t1, s1, (n + 1) & 1);
+      if (t2 < n_t) stat_store(s2);
       wait_tile_copies();
       __syncthreads();
       ++n;
-      i0 = i1;
-      i1 = i2;
+      t0 = t1;
+      t1 = t2;
     }
   };
   if (wave < 4) run(std::integral_constant<bool, true>{});
   else run(std::integral_constant<bool, false>{});
 
   // ---- epilogue: A writes dV, B writes dK = s dS^T Q (lane: key kw, dims 32 d0 + mrow)
-  if (kw < N) {
+  if (kw < lk) {
     const bool isA = wave < 4;
-    T* __restrict__ dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hoff + (size_t)kw * D;
+    T* __restrict__ dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
     const float sc = isA ? 1.f : p.scale;
 #pragma unroll
     for (int d0 = 0; d0 < DT32; ++d0)
@@ -555,19 +589,24 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 + l32;        // this lane's query
+  const int b = bh / p.H, h = bh - b * p.H;
+  const HeadView hv = head_view(p.L, b, h, p.H, N, D);
+  const int lq = hv.lq, lk = hv.lk;
+  if (q0 >= lq) return;                       // uniform: this block has no rows of its sequence
+  const int off = lk - lq;                    // causal: query i sees keys j <= i + off
 
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
-  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
-  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
-  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hoff, head_bytes);
+  const uint32_t q_bytes = span_bytes(lq, hv.q_stride, D, 2), kv_bytes = span_bytes(lk, hv.kv_stride, D, 2);
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hv.q_off, q_bytes);
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hv.kv_off, kv_bytes);
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hv.kv_off, kv_bytes);
+  const auto do_rs = make_rsrc(reinterpret_cast<const T*>(p.dO) + hv.q_off, q_bytes);
+  const int kv_rstride = hv.kv_stride * 2;
 
-  const int n_tiles = (N + BN - 1) / BN;
+  const int n_tiles = (lk + BN - 1) / BN;
   int j_end = n_tiles;
   if (p.causal) {
-    const int last_q = min(q0 + BM, N) - 1;
-    j_end = min(n_tiles, last_q / BN + 1);
+    const int last_vis = min(q0 + BM, lq) - 1 + off;
+    j_end = last_vis < 0 ? 0 : min(n_tiles, last_vis / BN + 1);
   }
   const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
   auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
@@ -577,14 +616,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   V8 qf[KC], of[KC];
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * D + 16 * c + 8 * g) * 2));
-    of[c] = as_v8<DT>(buf_load16(do_rs, (qw * D + 16 * c + 8 * g) * 2));
+    qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * hv.q_stride + 16 * c + 8 * g) * 2));
+    of[c] = as_v8<DT>(buf_load16(do_rs, (qw * hv.q_stride + 16 * c + 8 * g) * 2));
   }
-  float lse2 = INFINITY, dq_d = 0.f;          // rows past N or without a visible key: P = 0
-  if (qw < N) {
-    const float l = p.lse[(size_t)bh * N + qw];
+  float lse2 = INFINITY, dq_d = 0.f;          // rows past the sequence or without a visible key: P = 0
+  if (qw < lq) {
+    const size_t si = hv.stat_off + (size_t)qw * hv.stat_stride;
+    const float l = p.lse[si];
     if (l != -INFINITY) lse2 = l * kLog2e;
-    dq_d = p.Dvec[(size_t)bh * N + qw];
+    dq_d = p.Dvec[si];
   }
 
   int koff[KC];
@@ -596,18 +636,18 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     ktoff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
     ktoff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
-  const TileCopy<ROWB, TILE, NW> copy(wave, lane);
+  const TileCopy<ROWB, TILE, NW> copy(wave, lane, kv_rstride);
 
   f32x16 acc[DT32];
 #pragma unroll
   for (int t = 0; t < DT32; ++t) acc[t] = f32x16{};
   const float c2 = p.scale_log2;
 
-  // asynchronous copy of key tile j into LDS buffer buf (keys >= N arrive as zeros)
+  // asynchronous copy of key tile j into LDS buffer buf (keys past the sequence arrive as zeros)
   auto gload = [&](int j, int buf) {
     char* kt = smem + buf * 2 * TILE;
-    copy.issue(k_rs, kt, j * BN * D * 2);
-    copy.issue(v_rs, kt + TILE, j * BN * D * 2);
+    copy.issue(k_rs, kt, j * BN * kv_rstride);
+    copy.issue(v_rs, kt + TILE, j * BN * kv_rstride);
   };
 
   int j = next_kept(0);
@@ -622,7 +662,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
     const int k0 = j * BN;
-    const bool edge = (k0 + BN > N) || (p.causal && k0 + BN - 1 > q0);
+    const bool edge = (k0 + BN > lk) || (p.causal && k0 + BN - 1 > q0 + off);
 
 #pragma unroll
     for (int t = 0; t < NS; ++t) {
@@ -640,7 +680,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * t + mrow(g, r);
-          if (key >= N || (p.causal && key > qw)) de[r] = 0.f;
+          if (key >= lk || (p.causal && key > qw + off)) de[r] = 0.f;
         }
       }
 #pragma unroll
@@ -665,8 +705,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   }
 
   // ---- epilogue: lane holds query qw, dims 32 dt + mrow(g, r)
-  if (qw < N) {
-    T* __restrict__ dqg = reinterpret_cast<T*>(p.dq) + hoff + (size_t)qw * D;
+  if (qw < lq) {
+    T* __restrict__ dqg = reinterpret_cast<T*>(p.dq) + hv.q_off + (size_t)qw * hv.q_stride;
     const float sc = p.scale;
 #pragma unroll
     for (int dt = 0; dt < DT32; ++dt)
@@ -703,12 +743,12 @@ static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
   constexpr int NW = 4;
   constexpr int BM = NW * 32;
   p.q_blocks = (p.N + BM - 1) / BM;
-  p.k_blocks = (p.N + 127) / 128;
+  p.k_blocks = (p.L.Nk + 127) / 128;
   p.total_blocks = p.B * p.H * p.q_blocks;
   hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  p.total_blocks = p.B * p.H * p.k_blocks;
+  p.total_blocks = p.B * p.L.Hk * p.k_blocks;
   if constexpr (D == 64) {
     hipLaunchKernelGGL((dkdv_kernel<DT, D, 128, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   } else {

@@ -16,6 +16,8 @@
 
 #include <type_traits>
 
+#include "fa_launch.h"
+
 namespace fa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -204,9 +206,10 @@ __device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, int byt
 // instruction fills 1 KB of LDS: lane i's 16 bytes land at the wave's LDS
 // address + 16 i. A lane therefore fetches the global chunk that belongs at
 // its LDS slot under the row permutation; rows past the buffer range arrive as
-// zeros. The global tile is row-major with the same row length as the LDS
-// tile, and a wave's successive kilobytes are NW KB apart, a whole number of
-// swizzle periods, so one lane offset serves every chunk.
+// zeros. Global rows are row_stride bytes apart (the row length for a dense
+// head, heads x row length for a token-major packed tensor). A wave's
+// successive kilobytes are NW KB of LDS apart, a whole number of swizzle
+// periods, so one lane offset plus a fixed step serves every chunk.
 // Completion is tracked by vmcnt: wait_tile_copies() before the barrier that
 // publishes the tile.
 // ---------------------------------------------------------------------------
@@ -215,28 +218,75 @@ struct TileCopy {
   static constexpr int PER_WAVE = TILE_BYTES / (1024 * NW);
   static_assert(PER_WAVE * 1024 * NW == TILE_BYTES, "tile is a whole number of wave kilobytes");
   static_assert(((1024 * NW) / ROW_BYTES) % 16 == 0, "successive kilobytes are whole swizzle periods apart");
-  int goff;    // lane's global byte offset inside the tile for its first kilobyte
+  int goff;    // lane's global byte offset from the tile's first row, for its first kilobyte
+  int ustep;   // global byte step between this wave's successive kilobytes
   int wave;    // wave index (uniform)
-  __device__ __forceinline__ TileCopy(int wave_, int lane) {
+  __device__ __forceinline__ TileCopy(int wave_, int lane, int row_stride) {
     wave = __builtin_amdgcn_readfirstlane(wave_);
     const int p = 1024 * wave + 16 * lane;
     const int row = p / ROW_BYTES, slot = (p % ROW_BYTES) / 16;
-    goff = row * ROW_BYTES + ((slot ^ swz<ROW_BYTES>(row)) << 4);
+    goff = row * row_stride + ((slot ^ swz<ROW_BYTES>(row)) << 4);
+    ustep = (NW * 1024 / ROW_BYTES) * row_stride;
   }
-  // kilobyte u (0 <= u < PER_WAVE) of this wave's share only
+  // kilobyte u (0 <= u < PER_WAVE) of this wave's share only; gbase = byte
+  // offset of the tile's first row
   __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, char* tile, int gbase, int u) const {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)(tile + 1024 * (wave + NW * u)), 16,
-        goff + gbase + u * NW * 1024, 0, 0, 0);
+        goff + gbase + u * ustep, 0, 0, 0);
   }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char* tile, int gbase) const {
 #pragma unroll
-    for (int u = 0; u < PER_WAVE; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + 1024 * (wave + NW * u)), 16,
-          goff + gbase + u * NW * 1024, 0, 0, 0);
+    for (int u = 0; u < PER_WAVE; ++u) issue_one(rs, tile, gbase, u);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Rows of one (sequence, head): element offsets of row 0 in q/o, k/v and lse/D,
+// row counts and row strides, for the dense and the packed layouts.
+// ---------------------------------------------------------------------------
+struct HeadView {
+  size_t q_off, kv_off, stat_off;
+  int lq, lk;                                  // query / key rows (lq <= N, lk <= Nk)
+  int q_stride, kv_stride, stat_stride;        // elements between consecutive rows
+  size_t q_hstep, stat_hstep;                  // offset step to the next query head (same sequence)
+};
+__device__ __forceinline__ HeadView head_view(const SeqLayout& L, int b, int h, int H, int N, int D) {
+  HeadView v;
+  const int hk = h / (H / L.Hk);              // key/value head read by query head h
+  if (L.cu_q == nullptr) {
+    v.lq = N;
+    v.lk = L.Nk;
+    v.q_off = ((size_t)b * H + h) * (size_t)N * D;
+    v.kv_off = ((size_t)b * L.Hk + hk) * (size_t)L.Nk * D;
+    v.stat_off = ((size_t)b * H + h) * (size_t)N;
+    v.q_stride = D;
+    v.kv_stride = D;
+    v.stat_stride = 1;
+    v.q_hstep = (size_t)N * D;
+    v.stat_hstep = (size_t)N;
+  } else {
+    const int sq = min(max(L.cu_q[b], 0), L.total_q);
+    const int eq = min(max(L.cu_q[b + 1], sq), L.total_q);
+    const int sk = min(max(L.cu_k[b], 0), L.total_k);
+    const int ek = min(max(L.cu_k[b + 1], sk), L.total_k);
+    v.lq = min(eq - sq, N);                    // rows past the stated maximum are not computed
+    v.lk = min(ek - sk, L.Nk);
+    v.q_off = ((size_t)sq * H + h) * D;
+    v.kv_off = ((size_t)sk * L.Hk + hk) * D;
+    v.stat_off = (size_t)sq * H + h;
+    v.q_stride = H * D;
+    v.kv_stride = L.Hk * D;
+    v.stat_stride = H;
+    v.q_hstep = (size_t)D;
+    v.stat_hstep = 1;
+  }
+  return v;
+}
+// Byte range of `rows` rows of `width` elements, `stride` elements apart.
+__device__ __forceinline__ uint32_t span_bytes(int rows, int stride, int width, int elem_bytes) {
+  return rows > 0 ? (uint32_t)(((size_t)(rows - 1) * stride + width) * elem_bytes) : 0u;
+}
 
 // Wait until this wave's outstanding vector-memory operations (including the
 // tile copies above) have completed: s_waitcnt vmcnt(0).

@@ -56,19 +56,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 + l32;        // this lane's query row
+  const int b = bh / p.H, h = bh - b * p.H;
+  const HeadView hv = head_view(p.L, b, h, p.H, N, D);
+  const int lq = hv.lq, lk = hv.lk;
+  if (q0 >= lq) return;                       // uniform: this block has no rows of its sequence
+  const int off = lk - lq;                    // causal: query i sees keys j <= i + off
 
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hoff, head_bytes);
-  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hoff, head_bytes);
-  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hoff, head_bytes);
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hv.q_off, span_bytes(lq, hv.q_stride, D, 2));
+  const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hv.kv_off, span_bytes(lk, hv.kv_stride, D, 2));
+  const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hv.kv_off, span_bytes(lk, hv.kv_stride, D, 2));
+  const int kv_rstride = hv.kv_stride * 2;    // bytes between key rows
 
   // ---- key-tile range and skipping
-  const int n_tiles = (N + BN - 1) / BN;
+  const int n_tiles = (lk + BN - 1) / BN;
   int j_end = n_tiles;
   if (p.causal) {
-    const int last_q = min(q0 + BM, N) - 1;
-    j_end = min(n_tiles, last_q / BN + 1);
+    const int last_vis = min(q0 + BM, lq) - 1 + off;   // last key any row of this block sees
+    j_end = last_vis < 0 ? 0 : min(n_tiles, last_vis / BN + 1);
   }
   const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
   auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   // ---- Q fragments (B operand of S^T): lane holds Q[qw][16c + 8g .. +7]; rows >= N read as zero
   V8 qf[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * D + 16 * c + 8 * g) * 2));
+  for (int c = 0; c < KC; ++c) qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * hv.q_stride + 16 * c + 8 * g) * 2));
 
   // ---- lane-constant LDS offsets
   int koff[KC];                               // K operand: row l32, chunk 2c + g
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     voff[dt][0] = tr_off<ROWB>(4 * g, 32 * dt, lane);
     voff[dt][1] = tr_off<ROWB>(4 * g + 8, 32 * dt, lane);
   }
-  const TileCopy<ROWB, TILE, NW> copy(wave, lane);
+  const TileCopy<ROWB, TILE, NW> copy(wave, lane, kv_rstride);
 
   f32x16 acc[DT32];
 #pragma unroll
@@ -101,8 +105,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   // asynchronous copy of key tile j into LDS buffer buf (keys >= N arrive as zeros)
   auto gload = [&](int j, int buf) {
     char* kt = smem + buf * 2 * TILE;
-    copy.issue(k_rs, kt, j * BN * D * 2);
-    copy.issue(v_rs, kt + TILE, j * BN * D * 2);
+    copy.issue(k_rs, kt, j * BN * kv_rstride);
+    copy.issue(v_rs, kt + TILE, j * BN * kv_rstride);
   };
 
   int j = next_kept(0);
@@ -128,13 +132,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
       for (int c = 0; c < KC; ++c) s[t] = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s[t]);
     }
 
-    if ((k0 + BN > N) || (p.causal && k0 + BN - 1 > q0)) {
+    if ((k0 + BN > lk) || (p.causal && k0 + BN - 1 > q0 + off)) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * t + mrow(g, r);
-          if (key >= N || (p.causal && key > qw)) s[t][r] = -INFINITY;
+          if (key >= lk || (p.causal && key > qw + off)) s[t][r] = -INFINITY;
         }
     }
 
@@ -189,9 +193,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   // ---- epilogue: O = O~ / l, LSE = m ln2 + ln l
   {
     const float l_tot = pair_sum(l_run);
-    if (qw < N) {
+    if (qw < lq) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hoff + (size_t)qw * D;
+      T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hv.q_off + (size_t)qw * hv.q_stride;
 #pragma unroll
       for (int dt = 0; dt < DT32; ++dt)
 #pragma unroll
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
           *reinterpret_cast<u32x2*>(Og + 32 * dt + 8 * jj + 4 * g) = w;
         }
       if (g == 0) {
-        p.lse[(size_t)bh * N + qw] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
+        p.lse[hv.stat_off + (size_t)qw * hv.stat_stride] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
       }
     }
   }

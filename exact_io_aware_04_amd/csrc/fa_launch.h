@@ -6,6 +6,19 @@
 
 namespace fa {
 
+// Where the rows of one (sequence, head) live. Dense: [B, H, N, d] tensors,
+// cu_q == nullptr, Hk == H, Nk == N. Packed variable length: token-major
+// q/o [total_q, H, d], k/v [total_k, Hk, d], lse/D [total_q, H]; sequence b
+// owns rows cu_q[b] .. cu_q[b+1]-1 (clamped to [0, total_q]) and likewise for
+// keys; N and Nk are then the longest query / key sequence (grid extent).
+struct SeqLayout {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int Hk;
+  int Nk;
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -17,6 +30,7 @@ struct FwdParams {
   int mask_tiles;
   int causal;
   float scale_log2;      // softmax scale * log2(e)
+  SeqLayout L;
   int q_blocks;          // set by the launcher
   int total_blocks;      // set by the launcher
 };
@@ -37,6 +51,7 @@ struct BwdParams {
   int causal;
   float scale;
   float scale_log2;
+  SeqLayout L;
   int q_blocks;          // set by the launcher
   int k_blocks;          // set by the launcher
   int total_blocks;      // set by the launcher

@@ -6,9 +6,11 @@ stream. There is no fallback: if the shared library is missing or fails to
 load, importing this module raises.
 
 The low-level functions keep the C names (`fa_fwd`, `fa_bwd_preprocess`,
-`fa_bwd`, `fa_status_string`) and take integer
-device addresses. `forward` / `backward` are thin conveniences over torch
-tensors that allocate the outputs and call the same entry points.
+`fa_bwd`, `fa_fwd_varlen`, `fa_bwd_varlen`, `fa_status_string`) and take
+integer device addresses. `forward` / `backward` (dense [B, H, N, d]) and
+`forward_varlen` / `backward_varlen` (packed token-major, grouped heads) are
+thin conveniences over torch tensors that allocate the outputs and call the
+same entry points.
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE",
 }
-EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_status_string")
 
 
 def _load() -> ctypes.CDLL:
@@ -48,6 +50,10 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i]
     return lib
@@ -77,6 +83,18 @@ def fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block
            stream) -> int:
     return _lib.fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask,
                        mask_block, stream)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
+                  scale, causal, stream) -> int:
+    return _lib.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d,
+                              dt, scale, causal, stream)
+
+
+def fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk,
+                  d, dt, scale, causal, stream) -> int:
+    return _lib.fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q,
+                              max_k, Hq, Hk, d, dt, scale, causal, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -157,4 +175,56 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
                 float(scale), int(bool(causal)), _ptr(block_mask), mask_block, s)
     _check(st, "fa_bwd")
+    return dq, dk, dv, D
+
+
+def _varlen_shapes(q, k, v, cu_q, cu_k):
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("expected contiguous token-major [total, heads, d] tensors")
+    if tuple(v.shape) != tuple(k.shape) or k.dtype != q.dtype or v.dtype != q.dtype or k.shape[2] != q.shape[2]:
+        raise ValueError("k and v must share shape [total_k, Hk, d] and q's dtype and d")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or c.device != q.device:
+            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch + 1 offsets")
+    return int(cu_q.numel() - 1), int(q.shape[0]), int(k.shape[0]), int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   scale: Optional[float] = None, causal: bool = False, stream=None):
+    """fa_fwd_varlen on packed tensors q [total_q, Hq, d], k/v [total_k, Hk, d];
+    returns (o [total_q, Hq, d], lse [total_q, Hq])."""
+    torch = _torch()
+    batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q),
+                       int(max_seqlen_k), hq, hk, d, _dt(q), float(scale), int(bool(causal)), _stream(stream))
+    _check(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    scale: Optional[float] = None, causal: bool = False, stream=None):
+    """fa_bwd_preprocess over the packed rows, then fa_bwd_varlen; returns (dq, dk, dv, D)."""
+    torch = _torch()
+    batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = _dt(q)
+    s = _stream(stream)
+    D = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    if tq > 0:
+        _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), 1, hq, tq, d, dt, s), "fa_bwd_preprocess")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                       cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hk, d,
+                       dt, float(scale), int(bool(causal)), s)
+    _check(st, "fa_bwd_varlen")
     return dq, dk, dv, D

@@ -89,6 +89,50 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO,
                  int B, int H, int N, int d, fa_dtype dt, float scale,
                  int causal, const uint8_t* block_mask, int mask_block, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Packed variable-length batches with grouped key/value heads
+ * [P2, usage section: "padding and shapes" (variable-length sequences packed
+ * through cumulative offsets, no padding) and the library-interface list
+ * (multi-query / grouped-query attention); P1 key designs 1-3 for the
+ * operator itself].
+ *
+ *   q, o, dO, dq: token-major [total_q, Hq, d]; k, v, dk, dv: [total_k, Hk, d];
+ *   lse, D: float32 [total_q, Hq]. Hq must be a multiple of Hk; query head h
+ *   reads key/value head h / (Hq / Hk) (Hk == 1: multi-query attention).
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32 arrays of batch + 1 cumulative
+ *   offsets; sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1. The kernels clamp
+ *   every offset to [0, total] (so malformed offsets cannot address outside
+ *   the tensors), and rows of a sequence beyond max_seqlen_q / max_seqlen_k
+ *   are not computed: the caller passes the true maxima.
+ *   causal != 0 with n_q queries and n_k keys in a sequence: query i sees key
+ *   j iff j <= i + (n_k - n_q), i.e. the queries are the last n_q positions
+ *   of the key sequence (a reading: the pages only note that one backend
+ *   refuses causal attention with unequal lengths). Queries that see no key
+ *   get O = 0, LSE = -inf and no gradient; sequences with no query rows leave
+ *   their keys' dk, dv at zero.
+ *   Limits (FA_ERR_SHAPE otherwise): batch, max_seqlen_*, Hq, Hk >= 1,
+ *   total_* >= 0, max_seqlen_q * Hq * d * 2 and max_seqlen_k * Hk * d * 2
+ *   below 2^31. No block mask on this path. Otherwise the conventions of the
+ *   dense entry points apply (device pointers, 16-byte alignment, no
+ *   allocation, stream-ordered, validation before any HIP call).
+ *   D for fa_bwd_varlen comes from fa_bwd_preprocess(o, dO, D, 1, Hq,
+ *   total_q, d, dt, stream): the packed rows are contiguous in the same order.
+ * ------------------------------------------------------------------------ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                        int causal, void* stream);
+
+/* Gradients for fa_fwd_varlen. dk, dv of a key/value head sum the
+ * contributions of every query head that reads it (computed inside one
+ * workgroup per key block, no atomics: deterministic). */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                        const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                        int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                        void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -81,6 +81,41 @@ def test_bwd_validation(kw, code):
     assert bwd(**kw) == code
 
 
+def fwd_varlen(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, cu_q=A, cu_k=A, batch=2, total_q=40, total_k=50, max_q=30, max_k=30,
+                Hq=4, Hk=2, d=64, dt=fa.FA_BF16, scale=0.125, causal=1, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_varlen(*args.values())
+
+
+def bwd_varlen(**kw):
+    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, cu_q=A, cu_k=A, batch=2, total_q=40,
+                total_k=50, max_q=30, max_k=30, Hq=4, Hk=2, d=128, dt=fa.FA_F16, scale=0.125, causal=0,
+                stream=None)
+    args.update(kw)
+    return fa.fa_bwd_varlen(*args.values())
+
+
+VARLEN_CASES = [
+    (dict(q=None), -1), (dict(cu_q=None), -1), (dict(cu_k=None), -1),
+    (dict(batch=0), -2), (dict(total_q=-1), -2), (dict(max_q=0), -2), (dict(max_k=0), -2),
+    (dict(Hq=3, Hk=2), -2), (dict(Hk=0), -2), (dict(max_q=1 << 20, Hq=64), -2), (dict(max_k=1 << 20, Hk=64), -2),
+    (dict(dt=3), -3), (dict(d=96), -4),
+    (dict(o=MIS), -6), (dict(scale=0.0), -8),
+]
+
+
+@pytest.mark.parametrize("kw,code", VARLEN_CASES)
+def test_fwd_varlen_validation(kw, code):
+    assert fwd_varlen(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [c for c in VARLEN_CASES if "o" not in c[0]] + [
+    (dict(dk=None), -1), (dict(D=None), -1), (dict(dv=MIS), -6)])
+def test_bwd_varlen_validation(kw, code):
+    assert bwd_varlen(**kw) == code
+
+
 def test_preprocess_validation():
     assert fa.fa_bwd_preprocess(None, A, A, 1, 1, 16, 64, 0, None) == -1
     assert fa.fa_bwd_preprocess(A, A, A, 1, 1, 0, 64, 0, None) == -2

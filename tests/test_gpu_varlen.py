@@ -1,0 +1,117 @@
+"""Packed variable-length batches with grouped key/value heads: HIP path
+(fa_fwd_varlen / fa_bwd_varlen through the binding) vs oracle/varlen.py.
+
+Length mixes span several tiles, ragged tails, more queries than keys (causal
+rows that see nothing), fewer queries than keys (decode-like rows), and empty
+sequences. Tolerances are those of the dense tests (tests/harness.py).
+"""
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle.varlen as ov
+from harness import GRAD_REL_TOL, O_TOL, LSE_TOL, from_dev, rel_fro, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (lengths_q, lengths_k, Hq, Hk)
+    "mixed_gqa": ([1, 17, 128, 129, 300], [1, 40, 128, 200, 300], 4, 2),
+    "more_q_than_k": ([200, 64], [50, 64], 2, 1),
+    "decode_like": ([1, 3, 16], [700, 257, 1024], 8, 2),
+    "empty_seqs": ([0, 90, 130, 5], [70, 0, 130, 300], 2, 2),
+    "mqa_long": ([513], [513], 8, 1),
+}
+
+
+def _dev_i32(a):
+    import torch
+    return torch.from_numpy(np.asarray(a, dtype=np.int32)).cuda()
+
+
+def run_varlen(pk: ai.PackedDrawn, hq, hk, scale, causal):
+    import torch
+    from exact_io_aware_04_amd import fa
+    q, k, v, do = (to_dev(getattr(pk, n), pk.dtype) for n in ("q", "k", "v", "do"))
+    cu_q, cu_k = _dev_i32(pk.cu_q), _dev_i32(pk.cu_k)
+    mq = int(max(1, np.diff(pk.cu_q).max()))
+    mk = int(max(1, np.diff(pk.cu_k).max()))
+    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal)
+    dq, dk, dv, D = fa.backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, scale, causal)
+    torch.cuda.synchronize()
+    return {"o": from_dev(o, pk.dtype), "lse": lse.double().cpu().numpy(), "dq": from_dev(dq, pk.dtype),
+            "dk": from_dev(dk, pk.dtype), "dv": from_dev(dv, pk.dtype), "D": D.double().cpu().numpy(),
+            "dev": (o, lse, dq, dk, dv)}
+
+
+def _check(res, ref, dtype, what):
+    o, lse = res["o"], res["lse"]
+    assert np.isfinite(o).all(), f"{what}: non-finite O"
+    err = float(np.abs(o - ref[0]).max())
+    assert err <= O_TOL[dtype], f"{what}: O error {err:.3e}"
+    live = np.isfinite(ref[1])
+    assert (np.isneginf(lse) == ~live).all(), f"{what}: LSE -inf pattern"
+    if live.any():
+        lerr = float(np.abs(lse[live] - ref[1][live]).max())
+        assert lerr <= LSE_TOL, f"{what}: LSE error {lerr:.3e}"
+    g = ov.backward(*ref[2])
+    for n, r in zip(("dq", "dk", "dv"), g[:3]):
+        assert np.isfinite(res[n]).all(), f"{what}: non-finite {n}"
+        e = rel_fro(res[n], r)
+        assert e <= GRAD_REL_TOL, f"{what}: {n} relative error {e:.3e}"
+    dref = (res["_do"] * o).sum(axis=2)
+    derr = float((np.abs(res["D"] - dref) / (1 + np.abs(dref))).max())
+    assert derr <= 1e-3, f"{what}: D error {derr:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [ai.F16, ai.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", list(CASES))
+def test_varlen_parity(case, d, dtype, causal):
+    lq, lk, hq, hk = CASES[case]
+    seed = 30_000 + 13 * list(CASES).index(case) + d + (1 if dtype == ai.BF16 else 0) + (2 if causal else 0)
+    say(f"[varlen] {case} d={d} {dtype} causal={causal} seed={seed}")
+    pk = ai.draw_packed(lq, lk, hq, hk, d, dtype, seed)
+    scale = 1.0 / np.sqrt(d)
+    res = run_varlen(pk, hq, hk, scale, causal)
+    q, k, v, do = (pk.f64(n) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = ov.forward(q, k, v, pk.cu_q, pk.cu_k, scale, causal)
+    res["_do"] = do
+    _check(res, (o_ref, lse_ref, (q, k, v, do, pk.cu_q, pk.cu_k, scale, causal)), dtype,
+           f"{case} d={d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_equal_lengths_match_dense_bitwise(d, causal):
+    """Equal lengths and Hk == Hq: the packed path must give the dense path's bits
+    (same kernels, same arithmetic order, other strides)."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    B, H, N = 3, 2, 200
+    say(f"[varlen-vs-dense] d={d} causal={causal}")
+    dr = ai.draw(B, H, N, d, ai.BF16, 777 + d + causal)
+    q, k, v, do = (to_dev(getattr(dr, n), dr.dtype) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, None, causal)
+    dq, dk, dv, D = fa.backward(q, k, v, o, lse, do, None, causal)
+    pk = lambda x: x.transpose(1, 2).contiguous().view(B * N, H, d)
+    cu = _dev_i32(np.arange(B + 1) * N)
+    o2, lse2 = fa.forward_varlen(pk(q), pk(k), pk(v), cu, cu, N, N, None, causal)
+    dq2, dk2, dv2, D2 = fa.backward_varlen(pk(q), pk(k), pk(v), o2, lse2, pk(do), cu, cu, N, N, None, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, pk(o))
+    assert torch.equal(lse2, lse.transpose(1, 2).contiguous().view(B * N, H))
+    for a, b_ in ((dq2, dq), (dk2, dk), (dv2, dv)):
+        assert torch.equal(a, pk(b_))
+
+
+def test_varlen_backward_deterministic():
+    import torch
+    lq, lk, hq, hk = CASES["mixed_gqa"]
+    pk = ai.draw_packed(lq, lk, hq, hk, 128, ai.BF16, 4242)
+    say("[varlen-determinism] mixed_gqa d=128 bf16 causal")
+    a = run_varlen(pk, hq, hk, 1 / np.sqrt(128), True)["dev"]
+    b = run_varlen(pk, hq, hk, 1 / np.sqrt(128), True)["dev"]
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
