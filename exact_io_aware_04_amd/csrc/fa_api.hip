@@ -120,6 +120,43 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_varlen");
 }
 
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                         int causal, int n_splits, float* o_partial, float* lse_partial, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !o_partial || !lse_partial)
+    return FA_ERR_NULL;
+  FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
+  if (n_splits < 1 || n_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
+  // group-packed rows (Hq / Hk heads x max_seqlen_q) index the grid in 32 bits
+  const long double blocks = (long double)batch * Hk * (((long double)(Hq / Hk) * max_seqlen_q + 127) / 128) * n_splits;
+  if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;
+  FA_TRY(check_dtype(dt));
+  FA_TRY(check_scale(scale));
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_partial) ||
+      !aligned16(lse_partial))
+    return FA_ERR_ALIGN;
+
+  fa::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.mask = nullptr;
+  p.B = batch; p.H = Hq; p.N = max_seqlen_q; p.D = d;
+  p.mask_tiles = 0;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.L.cu_q = cu_seqlens_q;
+  p.L.cu_k = cu_seqlens_k;
+  p.L.total_q = total_q;
+  p.L.total_k = total_k;
+  p.L.Hk = Hk;
+  p.L.Nk = max_seqlen_k;
+  p.o_part = o_partial;
+  p.lse_part = lse_partial;
+  p.n_splits = n_splits;
+  p.part_rows = (long long)total_q * Hq;
+  return hip_status(fa::launch_fwd_splitkv(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_splitkv");
+}
+
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N, int d, fa_dtype dt,
                             void* stream) {
   if (!o || !dO || !D) return FA_ERR_NULL;

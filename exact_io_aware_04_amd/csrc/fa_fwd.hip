@@ -30,7 +30,15 @@ namespace fa {
 // this (log2 units); between rescales probabilities stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <class DT, int D, int BN, int NW>
+// SPLIT = false: one workgroup = NW*32 query rows of one (sequence, head), all
+// kept key tiles; writes O and LSE.
+// SPLIT = true (split-KV, packed layout): the rows of a workgroup are the
+// group-packed rows r = hh * n_q + i of one (sequence, key/value head) (query
+// head hk * G + hh, query row i), so a key/value tile is read once for the G
+// query heads that share it (decode: n_q small); the kept key tiles of the
+// block are cut into n_splits contiguous ranges, one per workgroup, and each
+// writes its normalised partial O and LSE in fp32 for splitkv_merge_kernel.
+template <class DT, int D, int BN, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
@@ -50,19 +58,40 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int N = p.N;
 
-  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = logical % p.n_splits;
+    logical /= p.n_splits;
+  }
   const int bh = logical / p.q_blocks;
   int qb = logical - bh * p.q_blocks;
   if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
   const int q0 = qb * BM;
-  const int qw = q0 + wave * 32 + l32;        // this lane's query row
-  const int b = bh / p.H, h = bh - b * p.H;
-  const HeadView hv = head_view(p.L, b, h, p.H, N, D);
+  const int qw = q0 + wave * 32 + l32;        // this lane's row (split-KV: group-packed row)
+  const int HB = SPLIT ? p.L.Hk : p.H;        // heads the grid enumerates
+  const int b = bh / HB, hb = bh - b * HB;
+  const int G = SPLIT ? p.H / p.L.Hk : 1;     // query heads packed into the rows
+  const HeadView hv = head_view(p.L, b, SPLIT ? hb * G : hb, p.H, N, D);
   const int lq = hv.lq, lk = hv.lk;
-  if (q0 >= lq) return;                       // uniform: this block has no rows of its sequence
+  const int nrows = G * lq;
+  if (q0 >= nrows) return;                    // uniform: this block has no rows of its sequence
   const int off = lk - lq;                    // causal: query i sees keys j <= i + off
+  // this lane's query head (within the group) and row
+  const int hh = SPLIT ? (qw < nrows ? qw / lq : 0) : 0;
+  const int qi = SPLIT ? (qw < nrows ? qw - hh * lq : lq) : qw;
+  // first / last row index i of the block (a block that straddles two heads spans all of [0, lq))
+  int i_min = q0, i_max = min(q0 + BM, lq) - 1;
+  if constexpr (SPLIT) {
+    const int r_last = min(q0 + BM, nrows) - 1;
+    const int h_first = q0 / lq, h_last = r_last / lq;
+    i_min = h_first == h_last ? q0 - h_first * lq : 0;
+    i_max = h_first == h_last ? r_last - h_last * lq : lq - 1;
+  }
 
-  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hv.q_off, span_bytes(lq, hv.q_stride, D, 2));
+  const uint32_t q_span = SPLIT ? (uint32_t)(((size_t)(lq - 1) * hv.q_stride + (size_t)(G - 1) * hv.q_hstep + D) * 2)
+                                : span_bytes(lq, hv.q_stride, D, 2);
+  const auto q_rs = make_rsrc(reinterpret_cast<const T*>(p.q) + hv.q_off, q_span);
   const auto k_rs = make_rsrc(reinterpret_cast<const T*>(p.k) + hv.kv_off, span_bytes(lk, hv.kv_stride, D, 2));
   const auto v_rs = make_rsrc(reinterpret_cast<const T*>(p.v) + hv.kv_off, span_bytes(lk, hv.kv_stride, D, 2));
   const int kv_rstride = hv.kv_stride * 2;    // bytes between key rows
@@ -71,17 +100,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   const int n_tiles = (lk + BN - 1) / BN;
   int j_end = n_tiles;
   if (p.causal) {
-    const int last_vis = min(q0 + BM, lq) - 1 + off;   // last key any row of this block sees
+    const int last_vis = i_max + off;         // last key any row of this block sees
     j_end = last_vis < 0 ? 0 : min(n_tiles, last_vis / BN + 1);
+  }
+  int j_begin = 0;
+  if constexpr (SPLIT) {                      // this workgroup's share of the block's key tiles
+    const int chunk = (j_end + p.n_splits - 1) / p.n_splits;
+    j_begin = min(split * chunk, j_end);
+    j_end = min(j_begin + chunk, j_end);
   }
   const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
   auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
   auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
 
-  // ---- Q fragments (B operand of S^T): lane holds Q[qw][16c + 8g .. +7]; rows >= N read as zero
+  // ---- Q fragments (B operand of S^T): lane holds row qi of its head, d = 16c + 8g .. +7;
+  // rows past the sequence read as zero (split-KV: an offset past the buffer range)
+  const int qrow_off = SPLIT ? (qw < nrows ? (qi * hv.q_stride + hh * (int)hv.q_hstep) * 2 : 0x7ff00000)
+                             : qw * hv.q_stride * 2;
   V8 qf[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c) qf[c] = as_v8<DT>(buf_load16(q_rs, (qw * hv.q_stride + 16 * c + 8 * g) * 2));
+  for (int c = 0; c < KC; ++c) qf[c] = as_v8<DT>(buf_load16(q_rs, qrow_off + (16 * c + 8 * g) * 2));
 
   // ---- lane-constant LDS offsets
   int koff[KC];                               // K operand: row l32, chunk 2c + g
@@ -109,7 +147,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
     copy.issue(v_rs, kt + TILE, j * BN * kv_rstride);
   };
 
-  int j = next_kept(0);
+  int j = next_kept(j_begin);
   if (j < j_end) gload(j, 0);
   wait_tile_copies();
   __syncthreads();
@@ -132,13 +170,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
       for (int c = 0; c < KC; ++c) s[t] = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s[t]);
     }
 
-    if ((k0 + BN > lk) || (p.causal && k0 + BN - 1 > q0 + off)) {
+    if ((k0 + BN > lk) || (p.causal && k0 + BN - 1 > i_min + off)) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * t + mrow(g, r);
-          if (key >= lk || (p.causal && key > qw + off)) s[t][r] = -INFINITY;
+          if (key >= lk || (p.causal && key > qi + off)) s[t][r] = -INFINITY;
         }
     }
 
@@ -191,7 +229,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   }
 
   // ---- epilogue: O = O~ / l, LSE = m ln2 + ln l
-  {
+  if constexpr (SPLIT) {
+    const float l_tot = pair_sum(l_run);
+    if (qw < nrows) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const size_t prow = (size_t)split * p.part_rows + hv.stat_off + (size_t)hh * hv.stat_hstep +
+                          (size_t)qi * hv.stat_stride;
+      float* __restrict__ Op = p.o_part + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4 w = {acc[dt][4 * jj] * inv, acc[dt][4 * jj + 1] * inv, acc[dt][4 * jj + 2] * inv, acc[dt][4 * jj + 3] * inv};
+          *reinterpret_cast<f32x4*>(Op + 32 * dt + 8 * jj + 4 * g) = w;
+        }
+      if (g == 0) p.lse_part[prow] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
+    }
+  } else {
     const float l_tot = pair_sum(l_run);
     if (qw < lq) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -217,8 +271,72 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t st) {
   constexpr int BM = NW * 32;
   p.q_blocks = (p.N + BM - 1) / BM;
   p.total_blocks = p.B * p.H * p.q_blocks;
-  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV merge: per packed row r, LSE = log sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s, the (O, LSE) form of the mergeable softmax
+// state (page 1, key design 2; page 2, FA2 section: the saved statistic is
+// L = m + log l). Splits with no visible key carry LSE_s = -inf and weight 0.
+// D / 4 threads per row, one float4 of every partial per thread.
+// ---------------------------------------------------------------------------
+template <class DT, int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ o_part,
+                                                            const float* __restrict__ lse_part, void* o_,
+                                                            float* __restrict__ lse, long long rows, int n_splits) {
+  using T = typename DT::T;
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const long long r = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (r >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, lse_part[(size_t)s * rows + r]);
+  T* __restrict__ o = reinterpret_cast<T*>(o_) + (size_t)r * D + 4 * c4;
+  if (m == -INFINITY) {                       // no split saw a key
+    *reinterpret_cast<u32x2*>(o) = pack4<DT>(0.f, 0.f, 0.f, 0.f);
+    if (c4 == 0) lse[r] = -INFINITY;
+    return;
+  }
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_splits; ++s) {
+    const float l = lse_part[(size_t)s * rows + r];
+    const float w = __expf(l - m);            // exp(-inf) = 0 for empty splits
+    if (w == 0.f) continue;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(o_part + ((size_t)s * rows + r) * D + 4 * c4);
+    wsum += w;
+    acc += w * x;
+  }
+  const float inv = 1.f / wsum;
+  *reinterpret_cast<u32x2*>(o) = pack4<DT>(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (c4 == 0) lse[r] = m + __logf(wsum);
+}
+
+template <class DT, int D, int BN, int NW>
+static hipError_t launch_fwd_splitkv_t(const FwdParams& p0, hipStream_t st) {
+  FwdParams p = p0;
+  constexpr int BM = NW * 32;
+  const int G = p.H / p.L.Hk;
+  p.q_blocks = (int)(((long long)G * p.N + BM - 1) / BM);
+  p.total_blocks = p.B * p.L.Hk * p.q_blocks * p.n_splits;
+  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.part_rows == 0) return e;
+  constexpr int RPB = 256 / (D / 4);
+  const unsigned blocks = (unsigned)((p.part_rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL((splitkv_merge_kernel<DT, D>), dim3(blocks), dim3(256), 0, st, p.o_part, p.lse_part, p.o, p.lse,
+                     p.part_rows, p.n_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_splitkv(const FwdParams& p, int is_bf16, hipStream_t st) {
+  if (p.D == 64) {
+    return is_bf16 ? launch_fwd_splitkv_t<BF16, 64, 128, 4>(p, st) : launch_fwd_splitkv_t<F16, 64, 128, 4>(p, st);
+  }
+  return is_bf16 ? launch_fwd_splitkv_t<BF16, 128, 64, 4>(p, st) : launch_fwd_splitkv_t<F16, 128, 64, 4>(p, st);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {

@@ -31,6 +31,12 @@ struct FwdParams {
   int causal;
   float scale_log2;      // softmax scale * log2(e)
   SeqLayout L;
+  // split-KV form (packed layout only): partial results of split s for packed
+  // row r = token * H + head at o_part[(s * part_rows + r) * D], lse_part[s * part_rows + r]
+  float* o_part;
+  float* lse_part;
+  int n_splits;
+  long long part_rows;
   int q_blocks;          // set by the launcher
   int total_blocks;      // set by the launcher
 };
@@ -58,6 +64,7 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st);
+hipError_t launch_fwd_splitkv(const FwdParams& p, int is_bf16, hipStream_t st);
 hipError_t launch_bwd_preprocess(const void* o, const void* dO, float* Dvec, long long rows, int D,
                                  int is_bf16, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st);

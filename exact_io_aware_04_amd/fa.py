@@ -29,7 +29,9 @@ STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE",
 }
-EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_splitkv",
+            "fa_status_string")
+FA_MAX_SPLITS = 256
 
 
 def _load() -> ctypes.CDLL:
@@ -54,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, vp, vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i]
     return lib
@@ -95,6 +99,12 @@ def fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, t
                   d, dt, scale, causal, stream) -> int:
     return _lib.fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q,
                               max_k, Hq, Hk, d, dt, scale, causal, stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt, scale,
+                   causal, n_splits, o_partial, lse_partial, stream) -> int:
+    return _lib.fa_fwd_splitkv(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
+                               scale, causal, n_splits, o_partial, lse_partial, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -228,3 +238,28 @@ def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_
                        dt, float(scale), int(bool(causal)), s)
     _check(st, "fa_bwd_varlen")
     return dq, dk, dv, D
+
+
+def splitkv_workspace(total_q: int, hq: int, d: int, n_splits: int, device):
+    """Partial-result buffers for fa_fwd_splitkv: (o_partial, lse_partial) in float32."""
+    torch = _torch()
+    return (torch.empty((n_splits, total_q, hq, d), dtype=torch.float32, device=device),
+            torch.empty((n_splits, total_q, hq), dtype=torch.float32, device=device))
+
+
+def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, n_splits: int,
+                    scale: Optional[float] = None, causal: bool = False, workspace=None, stream=None):
+    """fa_fwd_splitkv on packed tensors; returns (o, lse) like forward_varlen."""
+    torch = _torch()
+    batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    opart, lpart = splitkv_workspace(tq, hq, d, n_splits, q.device) if workspace is None else workspace
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q),
+                        int(max_seqlen_k), hq, hk, d, _dt(q), float(scale), int(bool(causal)), int(n_splits),
+                        opart.data_ptr(), lpart.data_ptr(), _stream(stream))
+    _check(st, "fa_fwd_splitkv")
+    return o, lse

@@ -124,6 +124,26 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
                         int causal, void* stream);
 
+/* Split-KV forward [P1, key design 2 (mergeable softmax state) and its
+ * history/outlook section (the state as an associative reduction for long
+ * key/value caches in decode); P2, FA2 section (saved L = m + log l)].
+ * Same inputs, outputs and conventions as fa_fwd_varlen. Each (sequence,
+ * key/value head) processes the Hq / Hk query heads of its group together
+ * (their rows packed: a key/value tile is read once for the whole group), and
+ * the key tiles each row block sees are cut into n_splits contiguous ranges
+ * computed by separate workgroups. Split s writes its normalised partial
+ * output O_s (fp32) and LSE_s into caller-provided workspace; a second kernel
+ * merges them: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ *   o_partial:   float32 [n_splits, total_q, Hq, d]   (16-byte aligned)
+ *   lse_partial: float32 [n_splits, total_q, Hq]
+ *   1 <= n_splits <= FA_MAX_SPLITS, else FA_ERR_SHAPE.
+ * The result equals fa_fwd_varlen's up to floating-point rounding order. */
+#define FA_MAX_SPLITS 256
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                         int causal, int n_splits, float* o_partial, float* lse_partial, void* stream);
+
 /* Gradients for fa_fwd_varlen. dk, dv of a key/value head sum the
  * contributions of every query head that reads it (computed inside one
  * workgroup per key block, no atomics: deterministic). */

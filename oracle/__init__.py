@@ -26,6 +26,7 @@ from .attention import (  # noqa: F401
     forward,
     backward,
     backward_head_sampled,
+    merge_normalised,
     merge_softmax_blocks,
     softmax_block_state,
 )

@@ -238,3 +238,23 @@ def merge_softmax_blocks(state_a, state_b):
     ca = np.exp(ma - m)
     cb = np.exp(mb - m)
     return m, ca * la + cb * lb, ca[:, None] * oa + cb[:, None] * ob
+
+
+def merge_normalised(o_parts, lse_parts):
+    """Merge softmax results computed over disjoint key subsets, given as
+    normalised outputs O_s and log-sum-exps LSE_s (the state page 2's FA2
+    section saves, L = m + log l, in place of (m, l)): by page 1, key design 2,
+    with l_s = exp(LSE_s - m) up to the common factor e^m,
+      LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+    Subsets with no visible key have LSE_s = -inf and weight 0; a row with no
+    visible key at all gets O = 0, LSE = -inf. o_parts [S, R, d], lse_parts [S, R]."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    live = np.isfinite(m)
+    m_safe = np.where(live, m, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - m_safe[None, :]), 0.0)
+    tot = w.sum(axis=0)
+    lse = np.where(live, m_safe + np.log(np.where(live, tot, 1.0)), -np.inf)
+    o = np.where(live[:, None], (w[:, :, None] * o_parts).sum(axis=0) / np.where(live, tot, 1.0)[:, None], 0.0)
+    return o, lse

@@ -116,6 +116,21 @@ def test_bwd_varlen_validation(kw, code):
     assert bwd_varlen(**kw) == code
 
 
+def fwd_splitkv(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, cu_q=A, cu_k=A, batch=2, total_q=2, total_k=5000, max_q=1, max_k=4096,
+                Hq=8, Hk=2, d=128, dt=fa.FA_BF16, scale=0.125, causal=0, n_splits=8, o_part=A, lse_part=A,
+                stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", VARLEN_CASES + [
+    (dict(o_part=None), -1), (dict(lse_part=None), -1), (dict(n_splits=0), -2),
+    (dict(n_splits=fa.FA_MAX_SPLITS + 1), -2), (dict(lse_part=MIS), -6), (dict(o_part=MIS), -6)])
+def test_fwd_splitkv_validation(kw, code):
+    assert fwd_splitkv(**kw) == code
+
+
 def test_preprocess_validation():
     assert fa.fa_bwd_preprocess(None, A, A, 1, 1, 16, 64, 0, None) == -1
     assert fa.fa_bwd_preprocess(A, A, A, 1, 1, 0, 64, 0, None) == -2

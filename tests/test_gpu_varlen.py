@@ -115,3 +115,46 @@ def test_varlen_backward_deterministic():
     b = run_varlen(pk, hq, hk, 1 / np.sqrt(128), True)["dev"]
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+SPLIT_CASES = {
+    # name: (lengths_q, lengths_k, Hq, Hk)
+    "decode_gqa": ([1, 1, 1, 1], [700, 1500, 33, 4096], 8, 2),
+    "decode_q4_mha": ([4, 4, 2], [2048, 900, 64], 4, 4),
+    "prefill_mqa": ([300, 129], [300, 500], 4, 1),
+}
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 16, 64])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(64, ai.F16), (128, ai.BF16)])
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_splitkv_parity(case, d, dtype, causal, n_splits):
+    import torch
+    from exact_io_aware_04_amd import fa
+    lq, lk, hq, hk = SPLIT_CASES[case]
+    seed = 40_000 + 31 * list(SPLIT_CASES).index(case) + d + (2 if causal else 0) + n_splits
+    say(f"[splitkv] {case} d={d} {dtype} causal={causal} splits={n_splits} seed={seed}")
+    pk = ai.draw_packed(lq, lk, hq, hk, d, dtype, seed)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = (to_dev(getattr(pk, n), pk.dtype) for n in ("q", "k", "v"))
+    cu_q, cu_k = _dev_i32(pk.cu_q), _dev_i32(pk.cu_k)
+    mq, mk = int(max(lq)), int(max(lk))
+    ws = fa.splitkv_workspace(q.shape[0], hq, d, n_splits, q.device)
+    ws[0].fill_(float("nan"))                 # every partial a split owns must be written
+    ws[1].fill_(float("nan"))
+    o, lse = fa.forward_splitkv(q, k, v, cu_q, cu_k, mq, mk, n_splits, scale, causal, workspace=ws)
+    o_v, lse_v = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ov.forward(pk.f64("q"), pk.f64("k"), pk.f64("v"), pk.cu_q, pk.cu_k, scale, causal)
+    what = f"{case} d={d} {dtype} causal={causal} splits={n_splits}"
+    for oo, ll, tag in ((o, lse, "splitkv"), (o_v, lse_v, "varlen")):
+        og, lg = from_dev(oo, dtype), ll.double().cpu().numpy()
+        assert np.isfinite(og).all(), f"{what} {tag}: non-finite O"
+        err = float(np.abs(og - o_ref).max())
+        assert err <= O_TOL[dtype], f"{what} {tag}: O error {err:.3e}"
+        live = np.isfinite(lse_ref)
+        assert (np.isneginf(lg) == ~live).all(), f"{what} {tag}: LSE pattern"
+        lerr = float(np.abs(lg[live] - lse_ref[live]).max()) if live.any() else 0.0
+        assert lerr <= LSE_TOL, f"{what} {tag}: LSE error {lerr:.3e}"
+    assert not torch.isnan(ws[1]).any(), f"{what}: unwritten partial LSE"

@@ -156,3 +156,44 @@ def test_gradient_invariants_and_d_identity():
         np.testing.assert_allclose(dk[sk:ek].sum(axis=0), 0.0, atol=1e-12)
         dsum = (do[sq:eq] * live[sq:eq, :, None]).sum(axis=(0, 1))
         np.testing.assert_allclose(dv[sk:ek, 0].sum(axis=0), dsum, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cuts", [[0, 9], [0, 3, 9], [0, 1, 2, 5, 5, 9], [0, 8, 9]])
+def test_merge_of_key_subsets_equals_full(causal, cuts):
+    """Page 1, key design 2: results over disjoint key subsets merge into the
+    full softmax. Subsets a causal row cannot see carry LSE = -inf."""
+    rng = np.random.default_rng(17)
+    nq, nk, d = 4, 9, 6
+    q, k, v = rng.standard_normal((nq, d)), rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+    off = nk - nq
+    o_full, lse_full = oracle.forward_head(q, k, v, 0.6, causal, diag_offset=off)
+    parts_o, parts_l = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        keys = np.arange(a, b)
+        vis = np.ones((nq, keys.size), bool) if not causal else keys[None, :] <= np.arange(nq)[:, None] + off
+        sc = np.where(vis, 0.6 * q @ k[a:b].T, -np.inf)
+        m = sc.max(axis=1, initial=-np.inf)
+        live = np.isfinite(m)
+        e = np.where(vis, np.exp(sc - np.where(live, m, 0)[:, None]), 0.0)
+        ell = e.sum(axis=1)
+        parts_o.append(np.where(live[:, None], (e @ v[a:b]) / np.where(live, ell, 1)[:, None], 0.0))
+        parts_l.append(np.where(live, np.where(live, m, 0) + np.log(np.where(live, ell, 1)), -np.inf))
+    o, lse = oracle.merge_normalised(parts_o, parts_l)
+    np.testing.assert_allclose(o, o_full, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_full, rtol=1e-12)
+    if len(parts_o) > 1:   # the plain average of the partial outputs is not the merge
+        assert not np.allclose(np.mean(parts_o, axis=0), o_full)
+
+
+def test_merge_forms_agree():
+    """The (O, LSE) merge and the (m, l, O~) merge of page 3's block states agree."""
+    rng = np.random.default_rng(23)
+    s1, s2 = rng.standard_normal((3, 4)), rng.standard_normal((3, 5))
+    v1, v2 = rng.standard_normal((4, 2)), rng.standard_normal((5, 2))
+    m, ell, acc = oracle.merge_softmax_blocks(oracle.softmax_block_state(s1, v1), oracle.softmax_block_state(s2, v2))
+    a1, a2 = oracle.softmax_block_state(s1, v1), oracle.softmax_block_state(s2, v2)
+    o, lse = oracle.merge_normalised([a1[2] / a1[1][:, None], a2[2] / a2[1][:, None]],
+                                     [a1[0] + np.log(a1[1]), a2[0] + np.log(a2[1])])
+    np.testing.assert_allclose(o, acc / ell[:, None], rtol=1e-13)
+    np.testing.assert_allclose(lse, m + np.log(ell), rtol=1e-13)
