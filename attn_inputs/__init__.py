@@ -219,3 +219,37 @@ def length_mix(batch: int, max_len: int, seed: int, min_len: int = 1) -> np.ndar
     lens = rng.integers(min_len, max_len + 1, size=batch)
     lens[0] = max_len
     return lens.astype(np.int64)
+
+
+@dataclasses.dataclass(frozen=True)
+class PackedWorkload:
+    """A packed variable-length batch used to measure the grouped-head and
+    split-KV paths (synthetic: the pages fix no such workload).
+    decode: one query per sequence against a key/value cache of length
+    U[max_k/2, max_k]; otherwise query and key lengths are equal, U[max_q/8, max_q]."""
+    name: str
+    batch: int
+    hq: int
+    hk: int
+    d: int
+    dtype: str
+    causal: bool
+    max_q: int
+    max_k: int
+    decode: bool
+    seed: int
+    n_splits: int = 1
+    backward: bool = True
+
+    def lengths(self):
+        if self.decode:
+            return np.ones(self.batch, dtype=np.int64), length_mix(self.batch, self.max_k, self.seed, self.max_k // 2)
+        lens = length_mix(self.batch, self.max_q, self.seed, self.max_q // 8)
+        return lens, lens.copy()
+
+
+PACKED_WORKLOADS = {w.name: w for w in [
+    PackedWorkload("varlen_gqa_b16_hq32_hk8_max4096_d128_bf16", 16, 32, 8, 128, BF16, True, 4096, 4096, False, 2001),
+    PackedWorkload("decode_splitkv_b32_hq32_hk8_k16384_d128_bf16", 32, 32, 8, 128, BF16, True, 1, 16384, True, 2002,
+                   n_splits=8, backward=False),
+]}

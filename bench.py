@@ -10,7 +10,9 @@ enqueues the three C-ABI calls. Prints ONE JSON line on stdout.
 
 The default workload is the GPT-2-medium attention shape (batch 64, 16 heads,
 length 1024, head dim 64, fp16, dense). Other workload names come from
-attn_inputs.WORKLOADS.
+attn_inputs.WORKLOADS, and attn_inputs.PACKED_WORKLOADS (packed variable-length
+batches with grouped key/value heads: forward + backward through
+fa_fwd_varlen / fa_bwd_varlen, or decode through fa_fwd_splitkv).
 """
 from __future__ import annotations
 
@@ -101,6 +103,156 @@ def cpu_baseline(w, dr, budget_s: float):
     }
 
 
+def cpu_baseline_packed(w, pk, budget_s: float):
+    """The float64 oracle on whole sequences of the packed workload (all heads),
+    in order, until the budget is used; TFLOP/s under the same convention."""
+    import numpy as np
+    import oracle.varlen as ov
+    from exact_io_aware_04_amd import metrics
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:
+        threadpool_info = None
+    lq, lk = w.lengths()
+    q, k, v, do = (pk.f64(n) for n in ("q", "k", "v", "do")) if w.backward else (
+        pk.f64("q"), pk.f64("k"), pk.f64("v"), None)
+    done_pairs, t0, n_seq, elapsed = 0, time.perf_counter(), 0, 0.0
+    for b in range(w.batch):
+        sq, eq, sk, ek = (int(pk.cu_q[b]), int(pk.cu_q[b + 1]), int(pk.cu_k[b]), int(pk.cu_k[b + 1]))
+        cq, ck = np.array([0, eq - sq]), np.array([0, ek - sk])
+        ov.forward(q[sq:eq], k[sk:ek], v[sk:ek], cq, ck, 1.0 / math.sqrt(w.d), w.causal)
+        if w.backward:
+            ov.backward(q[sq:eq], k[sk:ek], v[sk:ek], do[sq:eq], cq, ck, 1.0 / math.sqrt(w.d), w.causal)
+        done_pairs += metrics.kept_pairs_varlen([eq - sq], [ek - sk], w.causal) * w.hq
+        n_seq += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s:
+            break
+    per_pair = 4 * w.d + (10 * w.d if w.backward else 0)
+    cores = None
+    if threadpool_info is not None:
+        cores = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
+    return {"value": round(done_pairs * per_pair / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores or 1),
+            "kind": "oracle",
+            "sample": (f"{n_seq} of {w.batch} sequences (all {w.hq} query heads), "
+                       f"{'forward+backward' if w.backward else 'forward'}, float64 oracle, {elapsed:.1f} s")}
+
+
+def bench_packed(args, w) -> int:
+    """Packed workloads: varlen forward + backward, or split-KV decode forward."""
+    import numpy as np
+    import torch
+    import attn_inputs as ai
+    from exact_io_aware_04_amd import fa, metrics
+    lq, lk = w.lengths()
+    log(f"[bench] drawing {w.name} ({int(lq.sum())} query / {int(lk.sum())} key rows)")
+    pk = ai.draw_packed(lq, lk, w.hq, w.hk, w.d, w.dtype, w.seed)
+    dev = torch.device("cuda:0")
+    tdt = torch.float16 if w.dtype == ai.F16 else torch.bfloat16
+    dt = fa.FA_F16 if w.dtype == ai.F16 else fa.FA_BF16
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+    q, k, v = up(pk.q), up(pk.k), up(pk.v)
+    do = up(pk.do) if w.backward else None
+    cu_q = torch.from_numpy(pk.cu_q).to(dev)
+    cu_k = torch.from_numpy(pk.cu_k).to(dev)
+    tq, tk = int(lq.sum()), int(lk.sum())
+    mq, mk = int(lq.max()), int(lk.max())
+    o = torch.empty_like(q)
+    lse = torch.empty((tq, w.hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    scale = 1.0 / math.sqrt(w.d)
+    causal = int(w.causal)
+    args_common = (cu_q.data_ptr(), cu_k.data_ptr(), w.batch, tq, tk, mq, mk, w.hq, w.hk, w.d, dt, scale, causal)
+    if w.decode:
+        opart, lpart = fa.splitkv_workspace(tq, w.hq, w.d, w.n_splits, dev)
+
+        def fwd():
+            return fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     *args_common, w.n_splits, opart.data_ptr(), lpart.data_ptr(), s)
+    else:
+        def fwd():
+            return fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    *args_common, s)
+    if w.backward:
+        Dv = torch.empty((tq, w.hq), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def bwd_pre():
+            return fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), Dv.data_ptr(), 1, w.hq, tq, w.d, dt, s)
+
+        def bwd():
+            return fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                    Dv.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *args_common, s)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        assert fwd() == 0
+        if w.backward:
+            assert bwd_pre() == 0 and bwd() == 0
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    log(f"[bench] timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        if w.backward:
+            bwd_pre()
+            e[2].record(stream)
+            bwd()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    pre_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K if w.backward else 0.0
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K if w.backward else 0.0
+
+    pairs = metrics.kept_pairs_varlen(lq, lk, w.causal) * w.hq
+    f_fwd, f_bwd = 4 * w.d * pairs, 10 * w.d * pairs
+    total = f_fwd + (f_bwd if w.backward else 0)
+    value = total / (ms_step * 1e-3) / 1e12
+    b_fwd, b_bwd = metrics.packed_bytes(tq, tk, w.hq, w.hk, w.d)
+    if w.decode:
+        achieved = b_fwd / (fwd_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "fa_fwd_splitkv", "achieved": round(achieved, 1),
+                    "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / metrics.MI355X_HBM_GBPS, 4),
+                    "traffic": None, "launch_ms": round(fwd_ms, 4), "bytes_per_launch": b_fwd}
+        metric = "decode forward (split-KV) HBM GB/s and TFLOP/s, packed GQA batch"
+    else:
+        achieved = f_bwd / (bwd_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "fa_bwd_varlen", "achieved": round(achieved, 2),
+                    "peak": metrics.MI355X_PEAK_DENSE_F16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / metrics.MI355X_PEAK_DENSE_F16_TFLOPS, 4), "traffic": None,
+                    "launch_ms": round(bwd_ms, 4), "flops_per_launch": f_bwd}
+        metric = "packed varlen GQA attention fwd+bwd TFLOP/s"
+    result = {
+        "metric": metric, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "Hq": w.hq, "Hk": w.hk, "d": w.d, "causal": w.causal,
+                   "total_q": tq, "total_k": tk, "max_q": mq, "max_k": mk, "n_splits": w.n_splits if w.decode else None,
+                   "backward": w.backward, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / metrics.MI355X_PEAK_DENSE_F16_TFLOPS, 2),
+        "phases_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
+        "bytes_model": {"algorithmic_fwd": b_fwd, "algorithmic_bwd": b_bwd},
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        log(f"[bench] oracle CPU baseline ({args.cpu_seconds:.0f} s budget)")
+        result["cpu_baseline"] = cpu_baseline_packed(w, pk, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,8 +273,10 @@ def main() -> int:
     import attn_inputs as ai
     from exact_io_aware_04_amd import fa, metrics
 
+    if args.workload in ai.PACKED_WORKLOADS:
+        return bench_packed(args, ai.PACKED_WORKLOADS[args.workload])
     if args.workload not in ai.WORKLOADS:
-        log(f"unknown workload {args.workload}; choose from {list(ai.WORKLOADS)}")
+        log(f"unknown workload {args.workload}; choose from {list(ai.WORKLOADS) + list(ai.PACKED_WORKLOADS)}")
         return 2
     w = ai.WORKLOADS[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d

@@ -62,3 +62,29 @@ def standard_attention_bytes(B: int, H: int, N: int, e: int = 2):
 def score_and_prob_bytes_per_head(N: int, e: int = 2) -> int:
     """Bytes to hold S and P of one head in HBM (page 2's memory example)."""
     return 2 * N * N * e
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches (grouped key/value heads)
+# ---------------------------------------------------------------------------
+def kept_pairs_varlen(lengths_q, lengths_k, causal: bool) -> int:
+    """Kept (query, key) pairs per query head summed over the sequences. Causal
+    with n_q queries and n_k keys: query i sees min(n_k, max(0, i + n_k - n_q + 1))
+    keys (the queries are the last n_q key positions)."""
+    total = 0
+    for nq, nk in zip(lengths_q, lengths_k):
+        nq, nk = int(nq), int(nk)
+        if not causal:
+            total += nq * nk
+        else:
+            i = np.arange(nq, dtype=np.int64)
+            total += int(np.clip(i + (nk - nq) + 1, 0, nk).sum())
+    return int(total)
+
+
+def packed_bytes(total_q: int, total_k: int, hq: int, hk: int, d: int, e: int = 2):
+    """(forward, backward incl. preprocess) minimum HBM bytes of a packed batch:
+    forward reads Q, K, V and writes O, LSE; backward reads Q, K, V, dO, O, LSE
+    and writes dQ, dK, dV, D (and reads D)."""
+    q_b, kv_b, st = total_q * hq * d * e, total_k * hk * d * e, total_q * hq * 4
+    return 2 * q_b + 2 * kv_b + st, 4 * q_b + 4 * kv_b + 3 * st

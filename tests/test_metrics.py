@@ -53,3 +53,14 @@ def test_byte_models():
     assert fwd == 4 * 2 ** 26 * 2 + 4 * 2 ** 20
     std_fwd, std_all = metrics.standard_attention_bytes(64, 16, 1024)
     assert round(std_fwd / 1e9, 2) == 8.59 and round(std_all / 1e9, 1) == 23.6
+
+
+def test_varlen_pair_count_matches_oracle_visibility():
+    import oracle
+    from exact_io_aware_04_amd import metrics
+    lq, lk = [1, 5, 9, 0, 7], [6, 5, 3, 4, 0]
+    for causal in (False, True):
+        brute = sum(int(oracle.kept_pairs(np.arange(a), np.arange(b), causal, None, 128, b - a).sum())
+                    for a, b in zip(lq, lk))
+        assert metrics.kept_pairs_varlen(lq, lk, causal) == brute
+    assert metrics.kept_pairs_varlen([1], [4096], True) == 4096      # decode: one query sees every key
