@@ -17,7 +17,11 @@ Pins (tests/test_oracle_pins.py) tie it to what the pages and the
 mathematics fix: the page-3 worked example, the two-block merge, row sums,
 identical keys, the causal first row, finite differences, the D identity,
 special cases, gradient invariants, mask reductions and permutation
-equivariance. No function here is "parity unpinned".
+equivariance. Packed variable-length batches are in oracle/varlen.py and
+dropout in oracle/dropout.py (tests/test_oracle_varlen.py,
+tests/test_oracle_dropout.py). The one "parity unpinned" item is the bit
+pattern of the dropout generator (Philox4x32-10): only its statistical
+properties are pinned, and the GPU must reproduce it bit for bit.
 """
 from .attention import (  # noqa: F401
     kept_pairs,
