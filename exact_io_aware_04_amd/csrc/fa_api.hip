@@ -54,6 +54,20 @@ fa_status check_varlen(int batch, int total_q, int total_k, int max_q, int max_k
   return FA_OK;
 }
 
+// Dropout parameters: p in [0, 1) (finite); the drop decision compares a
+// generator word with floor(p 2^32) and kept values are scaled by 1 / (1 - p).
+fa_status make_dropout(float p_drop, uint64_t seed, uint32_t offset, fa::Dropout* d) {
+  if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_DROPOUT;
+  d->on = 1;
+  const double t = floor((double)p_drop * 4294967296.0);
+  d->threshold = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  d->rescale = (float)(1.0 / (1.0 - (double)p_drop));
+  d->seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  d->seed_hi = (uint32_t)(seed >> 32);
+  d->offset = offset;
+  return FA_OK;
+}
+
 fa::SeqLayout dense_layout(int H, int N) {
   fa::SeqLayout L{};
   L.cu_q = nullptr;
@@ -73,9 +87,9 @@ fa::SeqLayout dense_layout(int H, int N) {
 
 extern "C" {
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                 int d, fa_dtype dt, float scale, int causal, const uint8_t* block_mask, int mask_block,
-                 void* stream) {
+static fa_status fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, fa_dtype dt, float scale, int causal, const uint8_t* block_mask, int mask_block,
+                           const fa::Dropout& drop, void* stream, const char* where) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   FA_TRY(check_shape(B, H, N, d));
   FA_TRY(check_dtype(dt));
@@ -91,7 +105,25 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.L = dense_layout(H, N);
-  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd");
+  p.drop = drop;
+  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), where);
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 int d, fa_dtype dt, float scale, int causal, const uint8_t* block_mask, int mask_block,
+                 void* stream) {
+  return fwd_dense(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, fa::Dropout{}, stream,
+                   "fa_fwd");
+}
+
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                         int d, fa_dtype dt, float scale, int causal, const uint8_t* block_mask, int mask_block,
+                         float p_drop, uint64_t seed, uint32_t offset, void* stream) {
+  fa::Dropout drop{};
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  FA_TRY(make_dropout(p_drop, seed, offset, &drop));
+  return fwd_dense(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, drop, stream,
+                   "fa_fwd_dropout");
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -168,9 +200,10 @@ fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int 
                     "fa_bwd_preprocess");
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* D,
-                 void* dq, void* dk, void* dv, int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
-                 const uint8_t* block_mask, int mask_block, void* stream) {
+static fa_status bwd_dense(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           const float* D, void* dq, void* dk, void* dv, int B, int H, int N, int d, fa_dtype dt,
+                           float scale, int causal, const uint8_t* block_mask, int mask_block,
+                           const fa::Dropout& drop, void* stream, const char* where) {
   if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv) return FA_ERR_NULL;
   FA_TRY(check_shape(B, H, N, d));
   FA_TRY(check_dtype(dt));
@@ -190,7 +223,26 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, co
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.L = dense_layout(H, N);
-  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_bwd");
+  p.drop = drop;
+  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), where);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* D,
+                 void* dq, void* dk, void* dv, int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
+                 const uint8_t* block_mask, int mask_block, void* stream) {
+  return bwd_dense(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask, mask_block,
+                   fa::Dropout{}, stream, "fa_bwd");
+}
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                         const float* D, void* dq, void* dk, void* dv, int B, int H, int N, int d, fa_dtype dt,
+                         float scale, int causal, const uint8_t* block_mask, int mask_block, float p_drop,
+                         uint64_t seed, uint32_t offset, void* stream) {
+  fa::Dropout drop{};
+  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv) return FA_ERR_NULL;
+  FA_TRY(make_dropout(p_drop, seed, offset, &drop));
+  return bwd_dense(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask, mask_block, drop,
+                   stream, "fa_bwd_dropout");
 }
 
 fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
@@ -236,6 +288,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_DROPOUT: return "FA_ERR_DROPOUT: dropout probability must satisfy 0 <= p < 1";
   }
   return "unknown fa_status";
 }

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const void* __restrict_
 template <int D>
 struct DkdvOccupancy { static constexpr int value = D <= 64 ? 2 : 1; };
 
-template <class DT, int D, int BQ, int NW>
+template <class DT, int D, int BQ, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
@@ -208,6 +208,15 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
           ta[d0][h] = tr_pair<DT>(ot, troff[d0][0] + rb, troff[d0][1] + rb);
           tb[d0][h] = tr_pair<DT>(qt, troff[d0][0] + rb, troff[d0][1] + rb);
         }
+      // dropout keep bits of (query q0 + 32 mq + mrow(g, r), key kw), one generator call each
+      uint32_t kmask = 0xFFFFu;
+      if constexpr (DROP) {
+        const uint32_t bhq = (uint32_t)(b * p.H + hk * grp + t / nspan);
+#pragma unroll 1
+        for (int r = 0; r < 16; ++r)          // rolled: one generator call live at a time
+          if (!keep1(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + mrow(g, r)), bhq, (uint32_t)kw & 3u))
+            kmask &= ~(1u << r);
+      }
       float pe[16], de[16];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -217,7 +226,8 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * jj + u;
           pe[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[u]));
-          de[r] = dp[r] - d4[u];
+          // dP = Z o (dO V^T), Z = M / (1 - p)
+          de[r] = (DROP ? (((kmask >> r) & 1) ? dp[r] * p.drop.rescale : 0.f) : dp[r]) - d4[u];
         }
       }
       if (edge) {
@@ -231,6 +241,10 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
       for (int r = 0; r < 16; ++r) de[r] *= pe[r];
       // B operands: slot i of half h <-> query 32 mq + 16 h + 8 (i / 4) + 4 g + i % 4
       V8 pb[2], sb[2];
+      if constexpr (DROP) {                   // dV uses the dropped P (rescaled in the epilogue)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pe[r] = ((kmask >> r) & 1) ? pe[r] : 0.f;
+      }
       pb[0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
       pb[1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
       sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
@@ -258,6 +272,7 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     T* __restrict__ dkg = reinterpret_cast<T*>(p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
     T* __restrict__ dvg = reinterpret_cast<T*>(p.dv) + hv.kv_off + (size_t)kw * hv.kv_stride;
     const float sc = p.scale;
+    const float sv = DROP ? p.drop.rescale : 1.f;
 #pragma unroll
     for (int d0 = 0; d0 < DT32; ++d0)
 #pragma unroll
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
         *reinterpret_cast<u32x2*>(dkg + col) =
             pack4<DT>(dk[d0][4 * jj] * sc, dk[d0][4 * jj + 1] * sc, dk[d0][4 * jj + 2] * sc, dk[d0][4 * jj + 3] * sc);
         *reinterpret_cast<u32x2*>(dvg + col) =
-            pack4<DT>(dv[d0][4 * jj], dv[d0][4 * jj + 1], dv[d0][4 * jj + 2], dv[d0][4 * jj + 3]);
+            pack4<DT>(dv[d0][4 * jj] * sv, dv[d0][4 * jj + 1] * sv, dv[d0][4 * jj + 2] * sv, dv[d0][4 * jj + 3] * sv);
       }
   }
 }
@@ -285,7 +300,9 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
 // buffers. dS uses the same rounded P that enters dV (an fp16/bf16 rounding of
 // P, inside the gradient tolerance).
 // ---------------------------------------------------------------------------
-template <class DT, int D, int BQ>
+// DROP: role A draws the dropout mask; the P it hands to role B carries the
+// mask in the sign bit (negative = dropped), its own dV operand is the dropped P.
+template <class DT, int D, int BQ, bool DROP>
 __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
@@ -433,11 +450,33 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
               if (kw >= lk || (p.causal && kw > q + off)) pe[r] = 0.f;
             }
           }
-          pb[mq][0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
-          pb[mq][1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+          if constexpr (DROP) {
+            const uint32_t bhq = (uint32_t)(b * p.H + hk * qgrp + t / nspan);
+            uint32_t kmask = 0xFFFFu;
+#pragma unroll 1
+            for (int r = 0; r < 16; ++r)      // rolled: one generator call live at a time
+              if (!keep1(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + mrow(g, r)), bhq, (uint32_t)kw & 3u))
+                kmask &= ~(1u << r);
+            float pd[16];
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-            lds_write16(pbuf, (((grp * MQ + mq) * 2 + h) * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[mq][h]));
+            for (int r = 0; r < 16; ++r) {
+              const bool keep = (kmask >> r) & 1;
+              pd[r] = keep ? pe[r] : 0.f;
+              pe[r] = keep ? pe[r] : -pe[r];
+            }
+            const V8 e0 = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+            const V8 e1 = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+            lds_write16(pbuf, (((grp * MQ + mq) * 2 + 0) * 64 + lane) * 16, __builtin_bit_cast(u32x4, e0));
+            lds_write16(pbuf, (((grp * MQ + mq) * 2 + 1) * 64 + lane) * 16, __builtin_bit_cast(u32x4, e1));
+            pb[mq][0] = pack8<DT>(pd[0], pd[1], pd[2], pd[3], pd[4], pd[5], pd[6], pd[7]);
+            pb[mq][1] = pack8<DT>(pd[8], pd[9], pd[10], pd[11], pd[12], pd[13], pd[14], pd[15]);
+          } else {
+            pb[mq][0] = pack8<DT>(pe[0], pe[1], pe[2], pe[3], pe[4], pe[5], pe[6], pe[7]);
+            pb[mq][1] = pack8<DT>(pe[8], pe[9], pe[10], pe[11], pe[12], pe[13], pe[14], pe[15]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              lds_write16(pbuf, (((grp * MQ + mq) * 2 + h) * 64 + lane) * 16, __builtin_bit_cast(u32x4, pb[mq][h]));
+          }
         } else {
           dp[mq] = s;
         }
@@ -485,7 +524,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
           for (int jj = 0; jj < 4; ++jj) {
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) de[4 * jj + u] = (dp[mq][4 * jj + u] - d4[u]) * pe[4 * jj + u];
+            for (int u = 0; u < 4; ++u) {
+              const int r = 4 * jj + u;
+              if constexpr (DROP) {               // sign bit = dropped; dP = Z o (dO V^T)
+                const bool keep = !__builtin_signbit(pe[r]);
+                const float pr = __builtin_fabsf(pe[r]);
+                de[r] = ((keep ? dp[mq][r] * p.drop.rescale : 0.f) - d4[u]) * pr;
+              } else {
+                de[r] = (dp[mq][r] - d4[u]) * pe[r];
+              }
+            }
           }
           bop[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
           bop[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
@@ -548,7 +596,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   if (kw < lk) {
     const bool isA = wave < 4;
     T* __restrict__ dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
-    const float sc = isA ? 1.f : p.scale;
+    const float sc = isA ? (DROP ? p.drop.rescale : 1.f) : p.scale;
 #pragma unroll
     for (int d0 = 0; d0 < DT32; ++d0)
 #pragma unroll
@@ -563,7 +611,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per block of NW*32 queries, looping over key tiles
 // ---------------------------------------------------------------------------
-template <class DT, int D, int BN, int NW>
+template <class DT, int D, int BN, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
@@ -683,6 +731,14 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
           if (key >= lk || (p.causal && key > qw + off)) de[r] = 0.f;
         }
       }
+      if constexpr (DROP) {                   // dP = Z o (dO V^T), Z = M / (1 - p)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t kb4 = keep4(p.drop, (uint32_t)((k0 + 32 * t + 8 * jj + 4 * g) >> 2), (uint32_t)qw, (uint32_t)bh);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dp[4 * jj + u] = ((kb4 >> u) & 1) ? dp[4 * jj + u] * p.drop.rescale : 0.f;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) de[r] *= dp[r] - dq_d;
       V8 sb[2];
@@ -745,14 +801,17 @@ static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
   p.q_blocks = (p.N + BM - 1) / BM;
   p.k_blocks = (p.L.Nk + 127) / 128;
   p.total_blocks = p.B * p.H * p.q_blocks;
-  hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  if (p.drop.on) hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  else hipLaunchKernelGGL((dq_kernel<DT, D, BN_DQ, NW, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.total_blocks = p.B * p.L.Hk * p.k_blocks;
   if constexpr (D == 64) {
-    hipLaunchKernelGGL((dkdv_kernel<DT, D, 128, NW>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+    if (p.drop.on) hipLaunchKernelGGL((dkdv_kernel<DT, D, 128, NW, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+    else hipLaunchKernelGGL((dkdv_kernel<DT, D, 128, NW, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   } else {
-    hipLaunchKernelGGL((dkdv_split_kernel<DT, D, 64>), dim3(p.total_blocks), dim3(512), 0, st, p);
+    if (p.drop.on) hipLaunchKernelGGL((dkdv_split_kernel<DT, D, 64, true>), dim3(p.total_blocks), dim3(512), 0, st, p);
+    else hipLaunchKernelGGL((dkdv_split_kernel<DT, D, 64, false>), dim3(p.total_blocks), dim3(512), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -288,6 +288,46 @@ __device__ __forceinline__ uint32_t span_bytes(int rows, int stride, int width, 
   return rows > 0 ? (uint32_t)(((size_t)(rows - 1) * stride + width) * elem_bytes) : 0u;
 }
 
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products and a
+// word permutation with xors of the key, the key advanced by a Weyl sequence
+// between rounds. Counter-based: the dropout mask is a pure function of
+// (counter, key), so the backward regenerates the forward's mask.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+// Keep bits of elements (bh, i, 4 c .. 4 c + 3): bit u set iff word u >= threshold.
+__device__ __forceinline__ uint32_t keep4(const Dropout& dr, uint32_t c, uint32_t i, uint32_t bh) {
+  const u32x4 w = philox4x32_10(c, i, bh, dr.offset, dr.seed_lo, dr.seed_hi);
+  return (uint32_t)(w[0] >= dr.threshold) | ((uint32_t)(w[1] >= dr.threshold) << 1) |
+         ((uint32_t)(w[2] >= dr.threshold) << 2) | ((uint32_t)(w[3] >= dr.threshold) << 3);
+}
+
+// Keep bit of element (bh, i, 4 c + sel).
+__device__ __forceinline__ bool keep1(const Dropout& dr, uint32_t c, uint32_t i, uint32_t bh, uint32_t sel) {
+  const u32x4 w = philox4x32_10(c, i, bh, dr.offset, dr.seed_lo, dr.seed_hi);
+  const uint32_t x = (sel & 2) ? ((sel & 1) ? w[3] : w[2]) : ((sel & 1) ? w[1] : w[0]);
+  return x >= dr.threshold;
+}
+
 // Wait until this wave's outstanding vector-memory operations (including the
 // tile copies above) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_tile_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }

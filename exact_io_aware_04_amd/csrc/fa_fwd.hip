@@ -38,7 +38,10 @@ constexpr float kRescaleThreshold = 8.0f;
 // query heads that share it (decode: n_q small); the kept key tiles of the
 // block are cut into n_splits contiguous ranges, one per workgroup, and each
 // writes its normalised partial O and LSE in fp32 for splitkv_merge_kernel.
-template <class DT, int D, int BN, int NW, bool SPLIT>
+// DROP: dropout on P after the softmax (dense layout, not with SPLIT): the row
+// sum uses the undropped probabilities, the product P V the dropped ones, and
+// the epilogue applies 1 / (1 - p) with the normalisation.
+template <class DT, int D, int BN, int NW, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
@@ -209,6 +212,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
       pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
       l_run = sum8<DT>(pb[t][0], l_run);
       l_run = sum8<DT>(pb[t][1], l_run);
+      if constexpr (DROP) {
+        // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u: one generator call per jj
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t kb4 = keep4(p.drop, (uint32_t)((k0 + 32 * t + 8 * jj + 4 * g) >> 2), (uint32_t)qw, (uint32_t)bh);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) e[4 * jj + u] = ((kb4 >> u) & 1) ? e[4 * jj + u] : 0.f;
+        }
+        pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+      }
     }
 
 #pragma unroll
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
   } else {
     const float l_tot = pair_sum(l_run);
     if (qw < lq) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? (DROP ? p.drop.rescale : 1.f) / l_tot : 0.f;
       T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hv.q_off + (size_t)qw * hv.q_stride;
 #pragma unroll
       for (int dt = 0; dt < DT32; ++dt)
@@ -271,7 +285,10 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t st) {
   constexpr int BM = NW * 32;
   p.q_blocks = (p.N + BM - 1) / BM;
   p.total_blocks = p.B * p.H * p.q_blocks;
-  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  if (p.drop.on)
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -322,7 +339,7 @@ static hipError_t launch_fwd_splitkv_t(const FwdParams& p0, hipStream_t st) {
   const int G = p.H / p.L.Hk;
   p.q_blocks = (int)(((long long)G * p.N + BM - 1) / BM);
   p.total_blocks = p.B * p.L.Hk * p.q_blocks * p.n_splits;
-  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, true, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.part_rows == 0) return e;
   constexpr int RPB = 256 / (D / 4);

@@ -19,6 +19,17 @@ struct SeqLayout {
   int Nk;
 };
 
+// Dropout on the probabilities (dense layout): element (head bh = b H + h,
+// query i, key j) is dropped iff word j % 4 of Philox4x32-10(counter =
+// (j / 4, i, bh, offset), key = (seed_lo, seed_hi)) is below threshold; kept
+// elements are scaled by rescale = 1 / (1 - p).
+struct Dropout {
+  int on;
+  uint32_t threshold;
+  float rescale;
+  uint32_t seed_lo, seed_hi, offset;
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -31,6 +42,7 @@ struct FwdParams {
   int causal;
   float scale_log2;      // softmax scale * log2(e)
   SeqLayout L;
+  Dropout drop;
   // split-KV form (packed layout only): partial results of split s for packed
   // row r = token * H + head at o_part[(s * part_rows + r) * D], lse_part[s * part_rows + r]
   float* o_part;
@@ -58,6 +70,7 @@ struct BwdParams {
   float scale;
   float scale_log2;
   SeqLayout L;
+  Dropout drop;
   int q_blocks;          // set by the launcher
   int k_blocks;          // set by the launcher
   int total_blocks;      // set by the launcher

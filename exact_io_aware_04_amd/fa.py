@@ -27,10 +27,10 @@ FA_BF16 = 1
 FA_OK = 0
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
-    -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE",
+    -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE", -9: "FA_ERR_DROPOUT",
 }
-EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_splitkv",
-            "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
+            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_status_string")
 FA_MAX_SPLITS = 256
 
 
@@ -52,6 +52,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, f, u64, u32, vp]
+    lib.fa_bwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, f, u64, u32, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen.restype = i
@@ -87,6 +92,18 @@ def fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block
            stream) -> int:
     return _lib.fa_bwd(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask,
                        mask_block, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, p_drop, seed, offset,
+                   stream) -> int:
+    return _lib.fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, dt, scale, causal, block_mask, mask_block, p_drop, seed,
+                               offset, stream)
+
+
+def fa_bwd_dropout(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask, mask_block, p_drop,
+                   seed, offset, stream) -> int:
+    return _lib.fa_bwd_dropout(q, k, v, dO, lse, D, dq, dk, dv, B, H, N, d, dt, scale, causal, block_mask,
+                               mask_block, p_drop, seed, offset, stream)
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
@@ -263,3 +280,38 @@ def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
                         opart.data_ptr(), lpart.data_ptr(), _stream(stream))
     _check(st, "fa_fwd_splitkv")
     return o, lse
+
+
+def forward_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, scale: Optional[float] = None,
+                    causal: bool = False, block_mask=None, mask_block: int = 128, stream=None):
+    """fa_fwd_dropout on [B, H, N, d] tensors; returns (o, lse)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, _dt(q),
+                        float(scale), int(bool(causal)), _ptr(block_mask), mask_block, float(p_drop), int(seed),
+                        int(offset), _stream(stream))
+    _check(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, lse, dO, p_drop: float, seed: int, offset: int = 0, scale: Optional[float] = None,
+                     causal: bool = False, block_mask=None, mask_block: int = 128, stream=None):
+    """fa_bwd_preprocess then fa_bwd_dropout (same p_drop, seed, offset as the forward); returns (dq, dk, dv, D)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = _dt(q)
+    s = _stream(stream)
+    D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), B, H, N, d, dt, s), "fa_bwd_preprocess")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, float(scale), int(bool(causal)),
+                        _ptr(block_mask), mask_block, float(p_drop), int(seed), int(offset), s)
+    _check(st, "fa_bwd_dropout")
+    return dq, dk, dv, D

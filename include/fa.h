@@ -59,7 +59,8 @@ typedef enum {
   FA_ERR_MASK = -5,     /* block_mask given with mask_block != 128 */
   FA_ERR_ALIGN = -6,    /* a tensor pointer is not 16-byte aligned */
   FA_ERR_HIP = -7,      /* a HIP launch reported an error */
-  FA_ERR_SCALE = -8     /* scale is not finite and > 0 */
+  FA_ERR_SCALE = -8,    /* scale is not finite and > 0 */
+  FA_ERR_DROPOUT = -9   /* dropout probability outside [0, 1) */
 } fa_status;
 
 /* Forward [P1 key designs 1-2; P3 forward process].
@@ -88,6 +89,33 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO,
                  const float* lse, const float* D, void* dq, void* dk, void* dv,
                  int B, int H, int N, int d, fa_dtype dt, float scale,
                  int causal, const uint8_t* block_mask, int mask_block, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dropout on the attention probabilities [P1, key design 2 table and key
+ * design 3: the forward keeps the generator state, not the mask, and the
+ * backward regenerates the mask].
+ *   O = (P o Z) V with Z = M / (1 - p_drop), M the keep mask, P the softmax
+ *   probabilities; lse is that of the scores (dropout acts after the softmax),
+ *   so fa_bwd_preprocess applies unchanged (D_i = dO_i . O_i still holds).
+ *   Mask: element (head bh = b*H + h, query i, key j) is dropped iff word
+ *   j % 4 of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
+ *   (j / 4, i, bh, offset) and key (seed mod 2^32, seed / 2^32) is below
+ *   floor(p_drop * 2^32). The same (p_drop, seed, offset) must be passed to
+ *   the forward and the backward; `offset` separates independent masks drawn
+ *   with one seed. Otherwise identical to fa_fwd / fa_bwd (dense layout,
+ *   causal, block mask). FA_ERR_DROPOUT unless 0 <= p_drop < 1; p_drop = 0
+ *   reproduces fa_fwd / fa_bwd bit for bit.
+ * ------------------------------------------------------------------------ */
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
+                         const uint8_t* block_mask, int mask_block, float p_drop, uint64_t seed,
+                         uint32_t offset, void* stream);
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* D, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, fa_dtype dt, float scale, int causal,
+                         const uint8_t* block_mask, int mask_block, float p_drop, uint64_t seed,
+                         uint32_t offset, void* stream);
 
 /* ------------------------------------------------------------------------
  * Packed variable-length batches with grouped key/value heads

@@ -81,6 +81,37 @@ def test_bwd_validation(kw, code):
     assert bwd(**kw) == code
 
 
+def fwd_dropout(**kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=16, d=64, dt=fa.FA_F16, scale=0.125, causal=0,
+                block_mask=None, mask_block=128, p=0.1, seed=1, offset=0, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_dropout(*args.values())
+
+
+def bwd_dropout(**kw):
+    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, B=1, H=1, N=16, d=64, dt=fa.FA_F16, scale=0.125,
+                causal=0, block_mask=None, mask_block=128, p=0.1, seed=1, offset=0, stream=None)
+    args.update(kw)
+    return fa.fa_bwd_dropout(*args.values())
+
+
+DROPOUT_CASES = [
+    (dict(q=None), -1), (dict(p=-0.1), -9), (dict(p=1.0), -9), (dict(p=float("nan")), -9), (dict(p=float("inf")), -9),
+    (dict(N=0), -2), (dict(d=32), -4), (dict(dt=5), -3), (dict(block_mask=A, mask_block=64), -5), (dict(lse=MIS), -6),
+    (dict(scale=0.0), -8),
+]
+
+
+@pytest.mark.parametrize("kw,code", DROPOUT_CASES)
+def test_fwd_dropout_validation(kw, code):
+    assert fwd_dropout(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", DROPOUT_CASES + [(dict(dk=None), -1), (dict(D=MIS), -6)])
+def test_bwd_dropout_validation(kw, code):
+    assert bwd_dropout(**kw) == code
+
+
 def fwd_varlen(**kw):
     args = dict(q=A, k=A, v=A, o=A, lse=A, cu_q=A, cu_k=A, batch=2, total_q=40, total_k=50, max_q=30, max_k=30,
                 Hq=4, Hk=2, d=64, dt=fa.FA_BF16, scale=0.125, causal=1, stream=None)
