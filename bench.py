@@ -58,7 +58,7 @@ def measured_traffic(workload: str, kernel: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(w, dr, budget_s: float):
+def cpu_baseline(w, dr, budget_s: float, pdrop: float = 0.0):
     """Time the float64 oracle on whole heads of the same workload until the
     budget is used (at least one head); scale to TFLOP/s with the same FLOP
     convention as the GPU figure."""
@@ -78,9 +78,16 @@ def cpu_baseline(w, dr, budget_s: float):
     for b in range(w.B):
         for h in range(w.H):
             q, k, v = (dr.f64(n, b, h) for n in "qkv")
-            oracle.forward_head(q, k, v, w.scale, w.causal, mask, 128)
-            if w.backward:
-                oracle.backward_head(q, k, v, dr.f64("do", b, h), w.scale, w.causal, mask, 128)
+            if pdrop > 0:
+                import oracle.dropout as od
+                od.forward_head(q, k, v, w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h, mask, 128)
+                if w.backward:
+                    od.backward_head(q, k, v, dr.f64("do", b, h), w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h,
+                                     mask, 128)
+            else:
+                oracle.forward_head(q, k, v, w.scale, w.causal, mask, 128)
+                if w.backward:
+                    oracle.backward_head(q, k, v, dr.f64("do", b, h), w.scale, w.causal, mask, 128)
             heads += 1
             elapsed = time.perf_counter() - t0
             if elapsed >= budget_s:
@@ -259,6 +266,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P for dense workloads (fa_fwd_dropout / fa_bwd_dropout); 0 = off")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
     args = ap.parse_args()
@@ -305,7 +314,12 @@ def main() -> int:
     causal = int(w.causal)
     scale = float(w.scale)
 
+    pdrop, dseed = float(args.dropout), 0x5EED
+
     def fwd():
+        if pdrop > 0:
+            return fa.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N,
+                                     d, dt, scale, causal, bmp, 128, pdrop, dseed, 0, s)
         return fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, dt,
                          scale, causal, bmp, 128, s)
 
@@ -313,6 +327,10 @@ def main() -> int:
         return fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), Dv.data_ptr(), B, H, N, d, dt, s)
 
     def bwd():
+        if pdrop > 0:
+            return fa.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                     Dv.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, scale,
+                                     causal, bmp, 128, pdrop, dseed, 0, s)
         return fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), Dv.data_ptr(),
                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, scale,
                          causal, bmp, 128, s)
@@ -370,7 +388,7 @@ def main() -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": measured_traffic(w.name, kern),
+        "traffic": measured_traffic(w.name, kern) if pdrop == 0 else None,
         "launch_ms": round(kms, 4),
         "flops_per_launch": kflops,
     }
@@ -391,7 +409,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-                   "block_mask": w.mask, "backward": w.backward, "parallelism": "single GPU"},
+                   "block_mask": w.mask, "backward": w.backward, "dropout": pdrop, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "phases_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
         "phase_tflops": {"fwd": round(fwd_tf, 2), "bwd": round(bwd_tf, 2) if bwd_tf else None},
@@ -401,7 +419,7 @@ def main() -> int:
     }
     if args.cpu_seconds > 0:
         log(f"[bench] oracle CPU baseline ({args.cpu_seconds:.0f} s budget)")
-        result["cpu_baseline"] = cpu_baseline(w, dr, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, dr, args.cpu_seconds, pdrop)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
