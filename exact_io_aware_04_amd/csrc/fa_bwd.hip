@@ -818,7 +818,7 @@ static hipError_t launch_bwd_t(const BwdParams& p0, hipStream_t st) {
 
 hipError_t launch_bwd(const BwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_bwd_t<BF16, 64, 128>(p, st) : launch_bwd_t<F16, 64, 128>(p, st);
+    return is_bf16 ? launch_bwd_t<BF16, 64, 64>(p, st) : launch_bwd_t<F16, 64, 64>(p, st);
   }
   return is_bf16 ? launch_bwd_t<BF16, 128, 64>(p, st) : launch_bwd_t<F16, 128, 64>(p, st);
 }

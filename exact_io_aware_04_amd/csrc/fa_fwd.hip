@@ -41,8 +41,13 @@ constexpr float kRescaleThreshold = 8.0f;
 // DROP: dropout on P after the softmax (dense layout, not with SPLIT): the row
 // sum uses the undropped probabilities, the product P V the dropped ones, and
 // the epilogue applies 1 / (1 - p) with the normalisation.
+// d = 64 with 64-key tiles fits three waves per SIMD (<= 168 VGPRs) unless the
+// dropout generator is inlined; d = 128 two.
+template <int D, bool DROP>
+struct FwdOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 3 : 2; };
+
 template <class DT, int D, int BN, int NW, bool SPLIT, bool DROP>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_kernel(FwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
   constexpr int NT = NW * 64;
@@ -351,14 +356,14 @@ static hipError_t launch_fwd_splitkv_t(const FwdParams& p0, hipStream_t st) {
 
 hipError_t launch_fwd_splitkv(const FwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_fwd_splitkv_t<BF16, 64, 128, 4>(p, st) : launch_fwd_splitkv_t<F16, 64, 128, 4>(p, st);
+    return is_bf16 ? launch_fwd_splitkv_t<BF16, 64, 64, 4>(p, st) : launch_fwd_splitkv_t<F16, 64, 64, 4>(p, st);
   }
   return is_bf16 ? launch_fwd_splitkv_t<BF16, 128, 64, 4>(p, st) : launch_fwd_splitkv_t<F16, 128, 64, 4>(p, st);
 }
 
 hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
-    return is_bf16 ? launch_fwd_t<BF16, 64, 128, 4>(p, st) : launch_fwd_t<F16, 64, 128, 4>(p, st);
+    return is_bf16 ? launch_fwd_t<BF16, 64, 64, 4>(p, st) : launch_fwd_t<F16, 64, 64, 4>(p, st);
   }
   return is_bf16 ? launch_fwd_t<BF16, 128, 64, 4>(p, st) : launch_fwd_t<F16, 128, 64, 4>(p, st);
 }
