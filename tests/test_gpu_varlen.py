@@ -158,3 +158,60 @@ def test_splitkv_parity(case, d, dtype, causal, n_splits):
         lerr = float(np.abs(lg[live] - lse_ref[live]).max()) if live.any() else 0.0
         assert lerr <= LSE_TOL, f"{what} {tag}: LSE error {lerr:.3e}"
     assert not torch.isnan(ws[1]).any(), f"{what}: unwritten partial LSE"
+
+
+def test_packed_bench_workload_sampled():
+    """The varlen GQA workload bench.py times, at full size: whole (sequence,
+    key/value group) blocks checked against the oracle (the two shortest
+    sequences and the longest one, one group each)."""
+    w = ai.PACKED_WORKLOADS["varlen_gqa_b16_hq32_hk8_max4096_d128_bf16"]
+    lq, lk = w.lengths()
+    say(f"[packed-full] {w.name} total_q={int(lq.sum())}")
+    pk = ai.draw_packed(lq, lk, w.hq, w.hk, w.d, w.dtype, w.seed)
+    scale = 1.0 / np.sqrt(w.d)
+    res = run_varlen(pk, w.hq, w.hk, scale, w.causal)
+    grp = w.hq // w.hk
+    order = np.argsort(lq)
+    qf, kf, vf, dof = pk.f64("q"), pk.f64("k"), pk.f64("v"), pk.f64("do")
+    for b, g in ((int(order[0]), 3), (int(order[1]), 0), (int(order[-1]), 7)):
+        sq, eq, sk, ek = (int(pk.cu_q[b]), int(pk.cu_q[b + 1]), int(pk.cu_k[b]), int(pk.cu_k[b + 1]))
+        say(f"[packed-full] seq {b} len {eq - sq} group {g}")
+        heads = list(range(g * grp, (g + 1) * grp))
+        q, do = qf[sq:eq][:, heads], dof[sq:eq][:, heads]
+        k, v = kf[sk:ek][:, [g]], vf[sk:ek][:, [g]]
+        cu_q, cu_k = np.array([0, eq - sq]), np.array([0, ek - sk])
+        o_ref, lse_ref = ov.forward(q, k, v, cu_q, cu_k, scale, w.causal)
+        dq, dk, dv, _ = ov.backward(q, k, v, do, cu_q, cu_k, scale, w.causal)
+        what = f"seq {b} (len {eq - sq}) group {g}"
+        err = float(np.abs(res["o"][sq:eq][:, heads] - o_ref).max())
+        assert err <= O_TOL[w.dtype], f"{what}: O error {err:.3e}"
+        assert float(np.abs(res["lse"][sq:eq][:, heads] - lse_ref).max()) <= LSE_TOL, what
+        for name, got, ref in (("dq", res["dq"][sq:eq][:, heads], dq), ("dk", res["dk"][sk:ek][:, [g]], dk),
+                               ("dv", res["dv"][sk:ek][:, [g]], dv)):
+            e = rel_fro(got, ref)
+            assert e <= GRAD_REL_TOL, f"{what}: {name} relative error {e:.3e}"
+
+
+def test_decode_bench_workload_sampled():
+    """The split-KV decode workload bench.py times, at full size, in its launch
+    configuration (8 splits): sampled sequences, all query heads."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    w = ai.PACKED_WORKLOADS["decode_splitkv_b32_hq32_hk8_k16384_d128_bf16"]
+    lq, lk = w.lengths()
+    say(f"[decode-full] {w.name} total_k={int(lk.sum())}")
+    pk = ai.draw_packed(lq, lk, w.hq, w.hk, w.d, w.dtype, w.seed)
+    scale = 1.0 / np.sqrt(w.d)
+    q, k, v = (to_dev(getattr(pk, n), pk.dtype) for n in ("q", "k", "v"))
+    cu_q, cu_k = _dev_i32(pk.cu_q), _dev_i32(pk.cu_k)
+    o, lse = fa.forward_splitkv(q, k, v, cu_q, cu_k, int(lq.max()), int(lk.max()), w.n_splits, scale, w.causal)
+    torch.cuda.synchronize()
+    og, lg = from_dev(o, w.dtype), lse.double().cpu().numpy()
+    qf, kf, vf = pk.f64("q"), pk.f64("k"), pk.f64("v")
+    for b in (0, 5, 31):
+        sq, eq, sk, ek = (int(pk.cu_q[b]), int(pk.cu_q[b + 1]), int(pk.cu_k[b]), int(pk.cu_k[b + 1]))
+        o_ref, lse_ref = ov.forward(qf[sq:eq], kf[sk:ek], vf[sk:ek], np.array([0, eq - sq]), np.array([0, ek - sk]),
+                                    scale, w.causal)
+        err = float(np.abs(og[sq:eq] - o_ref).max())
+        assert err <= O_TOL[w.dtype], f"seq {b}: O error {err:.3e}"
+        assert float(np.abs(lg[sq:eq] - lse_ref).max()) <= LSE_TOL, f"seq {b}: LSE"
