@@ -125,12 +125,21 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   const int i_begin = p.causal ? max(k0 - off, 0) / BQ : 0;
   const int nspan = max(n_qt - i_begin, 0);
   const int n_t = grp * nspan;
-  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;   // dense layout only
   auto tile_i = [&](int t) { return i_begin + t % nspan; };
-  auto kept = [&](int t) {
-    return mcol == nullptr || mcol[(size_t)((tile_i(t) * BQ) / 128) * p.mask_tiles] != 0;
+  // first kept flat tile >= t (n_t if none): the block-mask column of this key block
+  // (the mask comes with the dense layout only)
+  const TileMask mcol(p.mask ? p.mask + (k0 / 128) : nullptr, (size_t)p.mask_tiles, p.mask_tiles, lane);
+  auto next_kept = [&](int t) {
+    while (t < n_t) {
+      const int hh = t / nspan, i = tile_i(t);
+      const int r = (i * BQ) / 128, r2 = mcol.next(r);
+      if (r2 == r) return t;
+      const int i2 = (r2 * 128) / BQ;       // first query tile of the next kept row tile
+      if (i2 < n_qt) return hh * nspan + (i2 - i_begin);
+      t = (hh + 1) * nspan;                 // nothing left for this head
+    }
+    return n_t;
   };
-  auto next_kept = [&](int t) { while (t < n_t && !kept(t)) ++t; return t; };
 
   const TileCopy<ROWB, QTILE, NW> copy(wave, lane, q_rstride);
   float lse_r = 0.f, dd_r = 0.f;
@@ -363,12 +372,21 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   const int i_begin = p.causal ? max(k0 - off, 0) / BQ : 0;
   const int nspan = max(n_qt - i_begin, 0);
   const int n_t = qgrp * nspan;
-  const uint8_t* __restrict__ mcol = p.mask ? p.mask + (k0 / 128) : nullptr;   // dense layout only
   auto tile_i = [&](int t) { return i_begin + t % nspan; };
-  auto kept = [&](int t) {
-    return mcol == nullptr || mcol[(size_t)((tile_i(t) * BQ) / 128) * p.mask_tiles] != 0;
+  // first kept flat tile >= t (n_t if none): the block-mask column of this key block
+  // (the mask comes with the dense layout only)
+  const TileMask mcol(p.mask ? p.mask + (k0 / 128) : nullptr, (size_t)p.mask_tiles, p.mask_tiles, lane);
+  auto next_kept = [&](int t) {
+    while (t < n_t) {
+      const int hh = t / nspan, i = tile_i(t);
+      const int r = (i * BQ) / 128, r2 = mcol.next(r);
+      if (r2 == r) return t;
+      const int i2 = (r2 * 128) / BQ;       // first query tile of the next kept row tile
+      if (i2 < n_qt) return hh * nspan + (i2 - i_begin);
+      t = (hh + 1) * nspan;                 // nothing left for this head
+    }
+    return n_t;
   };
-  auto next_kept = [&](int t) { while (t < n_t && !kept(t)) ++t; return t; };
   auto q_of = [&](int t) { return hv.q_off + (size_t)(t / nspan) * hv.q_hstep; };
   auto stat_of = [&](int t) { return hv.stat_off + (size_t)(t / nspan) * hv.stat_hstep; };
 
@@ -656,9 +674,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     const int last_vis = min(q0 + BM, lq) - 1 + off;
     j_end = last_vis < 0 ? 0 : min(n_tiles, last_vis / BN + 1);
   }
-  const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
-  auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
-  auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
+  // first kept key tile >= j (j_end if none): the block-mask row of this query block
+  const TileMask mask_row(p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr, 1, p.mask_tiles, lane);
+  auto next_kept = [&](int j) {
+    if (j >= j_end) return j_end;
+    const int r = (j * BN) / 128, r2 = mask_row.next(r);
+    return r2 == r ? j : min((r2 * 128) / BN, j_end);
+  };
 
   // ---- per-query state: Q and dO fragments (B operands of S^T and dP^T), LSE, D
   V8 qf[KC], of[KC];

@@ -372,6 +372,45 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Kept flags of one row (or one column) of the 128 x 128 block mask, read once
+// per workgroup: bit k of lane l's register is the flag of tile 64 k + l
+// (tiles 0 .. 2047). next(r) finds the first kept tile >= r with one ballot per
+// 64 tiles instead of one memory round trip per tile; tiles past 2047 are read
+// from memory.
+// ---------------------------------------------------------------------------
+struct TileMask {
+  const uint8_t* base;   // nullptr: every tile kept
+  size_t stride;         // bytes between consecutive tiles' flags
+  int n;                 // tiles in the row / column
+  uint32_t bits;
+  __device__ __forceinline__ TileMask(const uint8_t* base_, size_t stride_, int n_, int lane)
+      : base(base_), stride(stride_), n(n_), bits(0u) {
+    if (base != nullptr) {
+      const int words = min((n + 63) >> 6, 32);
+      for (int k = 0; k < words; ++k) {
+        const int t = 64 * k + lane;
+        if (t < n && base[(size_t)t * stride] != 0) bits |= 1u << k;
+      }
+    }
+  }
+  // first kept tile >= r, n if none (call with all lanes of the wave active)
+  __device__ __forceinline__ int next(int r) const {
+    if (base == nullptr) return r;
+    while (r < n) {
+      const int k = r >> 6;
+      if (k >= 32) {
+        while (r < n && base[(size_t)r * stride] == 0) ++r;
+        return r;
+      }
+      const uint64_t w = __builtin_amdgcn_ballot_w64(((bits >> k) & 1u) != 0u) & (~0ull << (r & 63));
+      if (w != 0ull) return 64 * k + (int)__builtin_ctzll(w);
+      r = 64 * (k + 1);
+    }
+    return n;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Work-group ordering: workgroups are handed to the 8 XCDs round-robin, so the
 // hardware id is remapped to give each XCD a contiguous run of logical blocks
 // (neighbouring tiles of one head then share that XCD's L2).

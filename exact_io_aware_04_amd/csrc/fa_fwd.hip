@@ -117,9 +117,13 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
     j_begin = min(split * chunk, j_end);
     j_end = min(j_begin + chunk, j_end);
   }
-  const uint8_t* __restrict__ mrow_ptr = p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr;
-  auto kept = [&](int j) { return mrow_ptr == nullptr || mrow_ptr[(j * BN) / 128] != 0; };
-  auto next_kept = [&](int j) { while (j < j_end && !kept(j)) ++j; return j; };
+  // first kept key tile >= j (j_end if none): the block-mask row of this query block
+  const TileMask mask_row(p.mask ? p.mask + (size_t)(q0 / 128) * p.mask_tiles : nullptr, 1, p.mask_tiles, lane);
+  auto next_kept = [&](int j) {
+    if (j >= j_end) return j_end;
+    const int r = (j * BN) / 128, r2 = mask_row.next(r);
+    return r2 == r ? j : min((r2 * 128) / BN, j_end);
+  };
 
   // ---- Q fragments (B operand of S^T): lane holds row qi of its head, d = 16c + 8g .. +7;
   // rows past the sequence read as zero (split-KV: an offset past the buffer range)
