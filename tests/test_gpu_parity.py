@@ -74,6 +74,32 @@ def test_fully_masked_rows(causal, dtype):
     assert (res["dq"][0, 0, 128:256] == 0).all()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_mask_rows_longer_than_2048_tiles(d):
+    """A block mask with 2049 tiles per row: the kernels find kept tiles below
+    2048 from a per-workgroup bitmask and read the flags of tiles past it from
+    memory. Pairs of tiles form independent 256-key groups, so each group is a
+    dense attention problem the oracle computes on its own."""
+    n_tiles = 2049
+    n = 128 * n_tiles
+    t = np.arange(n_tiles)
+    mask = (t[:, None] // 2 == t[None, :] // 2).astype(np.uint8)
+    say(f"[mask 2049 tiles] N={n} d={d} f16")
+    dr = ai.draw(1, 1, n, d, ai.F16, 90_210 + d)
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, False, mask)
+    assert np.isfinite(res["o"]).all(), "unwritten output rows"
+    q, k, v, do = (dr.f64(name, 0, 0) for name in ("q", "k", "v", "do"))
+    for grp in (0, 511, 1023, 1024):
+        a, b = 256 * grp, min(256 * grp + 256, n)
+        o, lse = oracle.forward_head(q[a:b], k[a:b], v[a:b], scale, False)
+        dq, dk, dv, _ = oracle.backward_head(q[a:b], k[a:b], v[a:b], do[a:b], scale, False)
+        what = f"group {grp} (rows {a}..{b - 1})"
+        check_forward(res["o"][0, 0, a:b], res["lse"][0, 0, a:b], o, lse, ai.F16, what)
+        check_grads({"dq": res["dq"][0, 0, a:b], "dk": res["dk"][0, 0, a:b], "dv": res["dv"][0, 0, a:b]},
+                    {"dq": dq, "dk": dk, "dv": dv}, what)
+
+
 def test_forward_is_bitwise_deterministic():
     import torch
     from exact_io_aware_04_amd import fa
