@@ -82,7 +82,7 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int N = p.N;
 
-  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.k_blocks);
   const int bh = logical / p.k_blocks;        // (sequence, key/value head)
   const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
   const int k0 = kb * BK;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   const int grp = wave & 3;
   const int N = p.N;
 
-  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.k_blocks);
   const int bh = logical / p.k_blocks;        // (sequence, key/value head)
   const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
   const int k0 = kb * BK;
@@ -649,7 +649,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int N = p.N;
 
-  const int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.q_blocks);
   const int bh = logical / p.q_blocks;
   int qb = logical - bh * p.q_blocks;
   if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first

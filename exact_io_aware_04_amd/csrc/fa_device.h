@@ -411,14 +411,19 @@ struct TileMask {
 };
 
 // ---------------------------------------------------------------------------
-// Work-group ordering: workgroups are handed to the 8 XCDs round-robin, so the
-// hardware id is remapped to give each XCD a contiguous run of logical blocks
-// (neighbouring tiles of one head then share that XCD's L2).
+// Work-group ordering: workgroups are handed to the 8 XCDs round-robin
+// (hardware id hw goes to XCD hw % 8). Logical blocks come in chunks of
+// `chunk` consecutive ids (the blocks of one (sequence, head)); the remap deals
+// whole chunks to the XCDs in turn, so a chunk's blocks share one XCD's L2 and
+// run back to back there, while consecutive chunks (the heads of one sequence)
+// spread over all XCDs and sequences of different lengths load them evenly.
+// Ids past the last whole round of 8 chunks map to themselves.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_remap(int hw, int total) {
-  const int per = total >> 3, rem = total & 7;
+__device__ __forceinline__ int xcd_remap(int hw, int total, int chunk) {
+  const int round = 8 * chunk;
+  if (hw >= (total / round) * round) return hw;
   const int x = hw & 7, idx = hw >> 3;
-  return x * per + (x < rem ? x : rem) + idx;
+  return ((idx / chunk) * 8 + x) * chunk + idx % chunk;
 }
 
 

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int N = p.N;
 
-  int logical = xcd_remap(blockIdx.x, p.total_blocks);
+  int logical = xcd_remap(blockIdx.x, p.total_blocks, SPLIT ? p.q_blocks * p.n_splits : p.q_blocks);
   int split = 0;
   if constexpr (SPLIT) {
     split = logical % p.n_splits;
