@@ -217,14 +217,12 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
           ta[d0][h] = tr_pair<DT>(ot, troff[d0][0] + rb, troff[d0][1] + rb);
           tb[d0][h] = tr_pair<DT>(qt, troff[d0][0] + rb, troff[d0][1] + rb);
         }
-      // dropout keep bits of (query q0 + 32 mq + mrow(g, r), key kw), one generator call each
+      // dropout keep bits of (query q0 + 32 mq + mrow(g, r), key kw)
       uint32_t kmask = 0xFFFFu;
       if constexpr (DROP) {
         const uint32_t bhq = (uint32_t)(b * p.H + hk * grp + t / nspan);
-#pragma unroll 1
-        for (int r = 0; r < 16; ++r)          // rolled: one generator call live at a time
-          if (!keep1(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + mrow(g, r)), bhq, (uint32_t)kw & 3u))
-            kmask &= ~(1u << r);
+        // rows mrow(g, r) = 8 (r / 4) + 4 g + r % 4 of this sub-tile
+        kmask = keep16_quad(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + 4 * g), bhq, lane);
       }
       float pe[16], de[16];
 #pragma unroll
@@ -470,11 +468,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
           }
           if constexpr (DROP) {
             const uint32_t bhq = (uint32_t)(b * p.H + hk * qgrp + t / nspan);
-            uint32_t kmask = 0xFFFFu;
-#pragma unroll 1
-            for (int r = 0; r < 16; ++r)      // rolled: one generator call live at a time
-              if (!keep1(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + mrow(g, r)), bhq, (uint32_t)kw & 3u))
-                kmask &= ~(1u << r);
+            // rows mrow(g, r) = 8 (r / 4) + 4 g + r % 4 of this sub-tile
+            const uint32_t kmask = keep16_quad(p.drop, (uint32_t)kw >> 2, (uint32_t)(q0 + 32 * mq + 4 * g), bhq, lane);
             float pd[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {

@@ -321,11 +321,26 @@ __device__ __forceinline__ uint32_t keep4(const Dropout& dr, uint32_t c, uint32_
          ((uint32_t)(w[2] >= dr.threshold) << 2) | ((uint32_t)(w[3] >= dr.threshold) << 3);
 }
 
-// Keep bit of element (bh, i, 4 c + sel).
-__device__ __forceinline__ bool keep1(const Dropout& dr, uint32_t c, uint32_t i, uint32_t bh, uint32_t sel) {
-  const u32x4 w = philox4x32_10(c, i, bh, dr.offset, dr.seed_lo, dr.seed_hi);
-  const uint32_t x = (sel & 2) ? ((sel & 1) ? w[3] : w[2]) : ((sel & 1) ? w[1] : w[0]);
-  return x >= dr.threshold;
+// Keep bits of the 16 elements a lane holds in a key-per-lane accumulator:
+// column (key) 4 c + (lane & 3), rows i0 + 8 j + v for j, v in 0..3, as bit
+// 4 j + v. The four lanes of a quad hold keys 4 c .. 4 c + 3, which one
+// generator call covers, so each lane makes the call for row i0 + 8 j +
+// (lane & 3) and the quad exchanges the four keep bits of each call.
+template <int V>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, V * 0x55, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t keep16_quad(const Dropout& dr, uint32_t c, uint32_t i0, uint32_t bh, int lane) {
+  const uint32_t u = (uint32_t)lane & 3u;
+  uint32_t kmask = 0u;
+#pragma unroll 1
+  for (int j = 0; j < 4; ++j) {              // rolled: one generator call live at a time
+    const uint32_t b = keep4(dr, c, i0 + 8u * (uint32_t)j + u, bh);
+    const uint32_t row4 = ((quad_bcast<0>(b) >> u) & 1u) | (((quad_bcast<1>(b) >> u) & 1u) << 1) |
+                          (((quad_bcast<2>(b) >> u) & 1u) << 2) | (((quad_bcast<3>(b) >> u) & 1u) << 3);
+    kmask |= row4 << (4 * j);
+  }
+  return kmask;
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
