@@ -100,6 +100,31 @@ def test_mask_rows_longer_than_2048_tiles(d):
                     {"dq": dq, "dk": dk, "dv": dv}, what)
 
 
+@pytest.mark.parametrize("d,dtype,causal", [(64, ai.F16, False), (128, ai.BF16, True)])
+def test_random_mask_across_mask_words(d, dtype, causal):
+    """Random block mask over 130 tiles per row, so the kept-tile search crosses
+    the 64-tile words of the per-workgroup bitmask; rows in the tiles at the
+    word boundaries, and key columns there, against the oracle."""
+    n_tiles = 130
+    n = 128 * n_tiles
+    mask = ai.random_block_mask(n_tiles, 0.12, 7_130 + d)
+    say(f"[mask 130 tiles] N={n} d={d} {dtype} causal={causal}")
+    dr = ai.draw(1, 1, n, d, dtype, 7_131 + d)
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, causal, mask)
+    tiles = [0, 1, 62, 63, 64, 65, 127, 128, 129]
+    rows = np.array(sorted({128 * t + r for t in tiles for r in (0, 61, 127)}))
+    q, k, v, do = (dr.f64(name, 0, 0) for name in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.forward_head(q, k, v, scale, causal, mask, 128, rows=rows)
+    check_forward(res["o"][0, 0, rows], res["lse"][0, 0, rows], o_ref, lse_ref, dtype, "sampled rows")
+    say(f"[mask 130 tiles] oracle gradients at {rows.size} rows / columns")
+    dq, dk, dv, _ = oracle.backward_head_sampled(q, k, v, do, scale, causal, mask, 128, rows, rows)
+    check_grads({"dq": res["dq"][0, 0, rows], "dk": res["dk"][0, 0, rows], "dv": res["dv"][0, 0, rows]},
+                {"dq": dq, "dk": dk, "dv": dv}, "sampled rows / columns")
+    for name in ("o", "dq", "dk", "dv"):
+        assert np.isfinite(res[name]).all(), f"non-finite {name}"
+
+
 def test_forward_is_bitwise_deterministic():
     import torch
     from exact_io_aware_04_amd import fa
