@@ -125,6 +125,23 @@ def test_random_mask_across_mask_words(d, dtype, causal):
         assert np.isfinite(res[name]).all(), f"non-finite {name}"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_grid_with_partial_round_of_heads(causal):
+    """11 heads x 3 blocks per head: the first 8 heads are dealt to the XCDs
+    round-robin by head, the last 3 heads' blocks keep their order; every
+    head is compared whole against the oracle."""
+    B, H, n, d = 1, 11, 300, 64
+    say(f"[block order] B={B} H={H} N={n} d={d} causal={causal}")
+    dr = ai.draw(B, H, n, d, ai.F16, 4_711 + int(causal))
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, causal, None)
+    for h in range(H):
+        ref = _oracle_head(dr, 0, h, scale, causal, None)
+        what = f"head {h}"
+        check_forward(res["o"][0, h], res["lse"][0, h], ref["o"], ref["lse"], ai.F16, what)
+        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
+
+
 def test_forward_is_bitwise_deterministic():
     import torch
     from exact_io_aware_04_amd import fa
