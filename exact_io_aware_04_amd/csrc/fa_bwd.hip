@@ -63,10 +63,8 @@ template <class DT, int D, int BQ, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
-  constexpr int NT = NW * 64;
   constexpr int BK = NW * 32;                 // keys per workgroup
   constexpr int ROWB = D * 2;
-  constexpr int CPR = D / 8;
   constexpr int QTILE = BQ * ROWB;
   constexpr int KC = D / 16;
   constexpr int MQ = BQ / 32;                 // 32-query halves per tile
@@ -628,10 +626,8 @@ template <class DT, int D, int BN, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
-  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int ROWB = D * 2;
-  constexpr int CPR = D / 8;
   constexpr int TILE = BN * ROWB;
   constexpr int KC = D / 16;
   constexpr int NS = BN / 32;

@@ -50,10 +50,8 @@ template <class DT, int D, int BN, int NW, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_kernel(FwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
-  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   constexpr int ROWB = D * 2;                 // bytes per K/V row
-  constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = BN * ROWB;
   constexpr int KC = D / 16;                  // contraction chunks over d
   constexpr int NS = BN / 32;                 // 32-key sub-tiles per tile
