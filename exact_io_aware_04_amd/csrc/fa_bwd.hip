@@ -155,7 +155,8 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
       const float l = q < lq ? p.lse[si] : -INFINITY;
       // rows past the sequence or with no visible key get P = exp2(s - inf) = 0
       lse_r = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dd_r = q < lq ? p.Dvec[si] : 0.f;
+      // stored as -D (1 - p): the dP accumulator starts from it (p = 0 without dropout)
+      dd_r = q < lq ? -p.Dvec[si] / (DROP ? p.drop.rescale : 1.f) : 0.f;
     }
   };
   auto sstore = [&](int buf) {
@@ -199,7 +200,15 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
         qa[c] = as_v8<DT>(lds_read16(qt, qoff[c] + 32 * mq * ROWB));
         oa[c] = as_v8<DT>(lds_read16(ot, qoff[c] + 32 * mq * ROWB));
       }
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // dP starts from -D (1 - p) (rows 8 jj + 4 g + u in register 4 jj + u), so
+      // that the chain ends at dP - D (1 - p) without a subtraction per element
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dp[4 * jj + u] = d4[u];
+      }
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         s = DT::mma(qa[c], kf[c], s);
@@ -226,13 +235,15 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + 32 * mq + 8 * jj + 4 * g);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
+        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * jj + u;
           pe[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -l4[u]));
-          // dP = Z o (dO V^T), Z = M / (1 - p)
-          de[r] = (DROP ? (((kmask >> r) & 1) ? dp[r] * p.drop.rescale : 0.f) : dp[r]) - d4[u];
+          // dP - D with dP = Z o (dO V^T), Z = M / (1 - p): kept (dO V^T - D (1 - p)) / (1 - p),
+          // dropped -D
+          de[r] = DROP ? (((kmask >> r) & 1) ? dp[r] : d4[u]) * p.drop.rescale : dp[r];
         }
       }
       if (edge) {
@@ -414,7 +425,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
       const int q = i_ld * BQ + tid;
       // rows past N or with no visible key get P = exp2(s - inf) = 0
       lse_s[slot * BQ + tid] = (q >= lq || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
-      dd_s[slot * BQ + tid] = q < lq ? dd_r : 0.f;
+      // stored as -D (1 - p): role B's dP accumulator starts from it (p = 0 without dropout)
+      dd_s[slot * BQ + tid] = q < lq ? -dd_r / (DROP ? p.drop.rescale : 1.f) : 0.f;
     }
   };
 
@@ -446,7 +458,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
         V8 xa[KC];
 #pragma unroll
         for (int c = 0; c < KC; ++c) xa[c] = as_v8<DT>(lds_read16(A ? qt : ot, qoff[c] + 32 * mq * ROWB));
+        // A: S from zero; B: dP from -D (1 - p) (rows 8 jj + 4 g + u in register 4 jj + u)
         f32x16 s = f32x16{};
+        if constexpr (!A) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd_s + slot * BQ + 32 * mq + 8 * jj + 4 * g);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[4 * jj + u] = d4[u];
+          }
+        }
 #pragma unroll
         for (int c = 0; c < KC; ++c) s = DT::mma(xa[c], kvf[c], s);
         if constexpr (A) {
@@ -533,16 +554,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
             unpack8<DT>(as_v8<DT>(lds_read16(pbuf, (((grp * MQ + mq) * 2 + h) * 64 + lane) * 16)), pe + 8 * h);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
+            f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(dl + 32 * mq + 8 * jj + 4 * g);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int r = 4 * jj + u;
               if constexpr (DROP) {               // sign bit = dropped; dP = Z o (dO V^T)
+                // kept: (dO V^T - D (1 - p)) / (1 - p) = dP - D; dropped: -D
                 const bool keep = !__builtin_signbit(pe[r]);
                 const float pr = __builtin_fabsf(pe[r]);
-                de[r] = ((keep ? dp[mq][r] * p.drop.rescale : 0.f) - d4[u]) * pr;
+                de[r] = ((keep ? dp[mq][r] : d4[u]) * p.drop.rescale) * pr;
               } else {
-                de[r] = (dp[mq][r] - d4[u]) * pe[r];
+                de[r] = dp[mq][r] * pe[r];
               }
             }
           }
