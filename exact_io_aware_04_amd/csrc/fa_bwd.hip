@@ -283,22 +283,16 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
     t = tn;
   }
 
-  // ---- epilogue: lane holds key kw, dims 32 d0 + mrow(g, r)
-  if (kw < lk) {
-    T* __restrict__ dkg = reinterpret_cast<T*>(p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
-    T* __restrict__ dvg = reinterpret_cast<T*>(p.dv) + hv.kv_off + (size_t)kw * hv.kv_stride;
-    const float sc = p.scale;
-    const float sv = DROP ? p.drop.rescale : 1.f;
-#pragma unroll
-    for (int d0 = 0; d0 < DT32; ++d0)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int col = 32 * d0 + 8 * jj + 4 * g;
-        *reinterpret_cast<u32x2*>(dkg + col) =
-            pack4<DT>(dk[d0][4 * jj] * sc, dk[d0][4 * jj + 1] * sc, dk[d0][4 * jj + 2] * sc, dk[d0][4 * jj + 3] * sc);
-        *reinterpret_cast<u32x2*>(dvg + col) =
-            pack4<DT>(dv[d0][4 * jj] * sv, dv[d0][4 * jj + 1] * sv, dv[d0][4 * jj + 2] * sv, dv[d0][4 * jj + 3] * sv);
-      }
+  // ---- epilogue: lane holds key kw, dims 32 d0 + mrow(g, r); rows kw0.. go out
+  // through this wave's part of the (now idle) tile buffers
+  static_assert(2 * NW * stage_bytes<D>() <= 4 * QTILE, "staging fits the tile buffers");
+  {
+    char* const st = smem + wave * 2 * stage_bytes<D>();
+    const int rows = min(32, lk - kw0);
+    const size_t row0 = hv.kv_off + (size_t)kw0 * hv.kv_stride;
+    store_tile_rows<DT, D>(dk, p.scale, st, reinterpret_cast<T*>(p.dk) + row0, hv.kv_stride, rows, lane);
+    store_tile_rows<DT, D>(dv, DROP ? p.drop.rescale : 1.f, st + stage_bytes<D>(), reinterpret_cast<T*>(p.dv) + row0,
+                           hv.kv_stride, rows, lane);
   }
 }
 
@@ -626,27 +620,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   if (wave < 4) run(std::integral_constant<bool, true>{});
   else run(std::integral_constant<bool, false>{});
 
-  // ---- epilogue: A writes dV, B writes dK = s dS^T Q (lane: key kw, dims 32 d0 + mrow)
-  if (kw < lk) {
+  // ---- epilogue: A writes dV, B writes dK = s dS^T Q (lane: key kw, dims 32 d0 + mrow);
+  // rows kw0.. go out through this wave's part of the (now idle) tile slots
+  static_assert(8 * stage_bytes<D>() <= 6 * QTILE, "staging fits the tile slots");
+  {
     const bool isA = wave < 4;
-    T* __restrict__ dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hv.kv_off + (size_t)kw * hv.kv_stride;
-    const float sc = isA ? (DROP ? p.drop.rescale : 1.f) : p.scale;
-#pragma unroll
-    for (int d0 = 0; d0 < DT32; ++d0)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int col = 32 * d0 + 8 * jj + 4 * g;
-        *reinterpret_cast<u32x2*>(dst + col) =
-            pack4<DT>(acc[d0][4 * jj] * sc, acc[d0][4 * jj + 1] * sc, acc[d0][4 * jj + 2] * sc, acc[d0][4 * jj + 3] * sc);
-      }
+    const int rows = min(32, lk - kw0);
+    T* const dst = reinterpret_cast<T*>(isA ? p.dv : p.dk) + hv.kv_off + (size_t)kw0 * hv.kv_stride;
+    store_tile_rows<DT, D>(acc, isA ? (DROP ? p.drop.rescale : 1.f) : p.scale, smem + wave * stage_bytes<D>(), dst,
+                           hv.kv_stride, rows, lane);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per block of NW*32 queries, looping over key tiles
 // ---------------------------------------------------------------------------
+// Register target: three waves per SIMD (<= 168 VGPRs) at d = 64 without
+// dropout, two otherwise.
+template <int D, bool DROP>
+struct DqOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 3 : 2; };
+
 template <class DT, int D, int BN, int NW, bool DROP>
-__global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_kernel(BwdParams p) {
   using T = typename DT::T;
   using V8 = typename DT::V8;
   constexpr int BM = NW * 32;
@@ -796,17 +791,12 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(BwdParams p) {
     j = jn;
   }
 
-  // ---- epilogue: lane holds query qw, dims 32 dt + mrow(g, r)
-  if (qw < lq) {
-    T* __restrict__ dqg = reinterpret_cast<T*>(p.dq) + hv.q_off + (size_t)qw * hv.q_stride;
-    const float sc = p.scale;
-#pragma unroll
-    for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<u32x2*>(dqg + 32 * dt + 8 * jj + 4 * g) =
-            pack4<DT>(acc[dt][4 * jj] * sc, acc[dt][4 * jj + 1] * sc, acc[dt][4 * jj + 2] * sc, acc[dt][4 * jj + 3] * sc);
-  }
+  // ---- epilogue: lane holds query qw, dims 32 dt + mrow(g, r); rows q0 + 32 wave..
+  // go out through this wave's part of the (now idle) tile buffers
+  static_assert(NW * stage_bytes<D>() <= 4 * TILE, "staging fits the tile buffers");
+  store_tile_rows<DT, D>(acc, p.scale, smem + wave * stage_bytes<D>(),
+                         reinterpret_cast<T*>(p.dq) + hv.q_off + (size_t)(q0 + wave * 32) * hv.q_stride, hv.q_stride,
+                         min(32, lq - (q0 + wave * 32)), lane);
 }
 
 // ---------------------------------------------------------------------------

@@ -442,4 +442,44 @@ __device__ __forceinline__ int xcd_remap(int hw, int total, int chunk) {
 }
 
 
+
+// ---------------------------------------------------------------------------
+// Store of a wave's 32-row output tile with whole rows per instruction. In the
+// MFMA accumulator layout lane l holds row l % 32 and, for each 32-column
+// block t, the columns 32 t + mrow(l / 32, r); storing that directly writes
+// 8-byte pieces of 32 different rows per instruction (32 L2 requests of 16
+// bytes each). The tile goes through a per-wave LDS area instead (rows padded
+// by 16 bytes) and is read back with 16 consecutive bytes of one row per lane,
+// so that each store instruction writes whole rows. `scale` multiplies this
+// lane's row before rounding; rows >= `rows` are not written.
+// stage: this wave's own LDS area of stage_bytes<W>() bytes, with no copy in
+// flight into it and no other wave using it.
+// ---------------------------------------------------------------------------
+template <int W>
+constexpr int stage_bytes() { return 32 * (2 * W + 16); }
+
+template <class DT, int W>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[W / 32], float scale, char* stage,
+                                                typename DT::T* __restrict__ g0, size_t row_stride, int rows,
+                                                int lane) {
+  constexpr int RS = 2 * W + 16;              // padded row: 16-byte aligned, rows 4 banks apart
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int t = 0; t < W / 32; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      lds_write8(stage, l32 * RS + (32 * t + 8 * jj + 4 * g) * 2,
+                 pack4<DT>(acc[t][4 * jj] * scale, acc[t][4 * jj + 1] * scale, acc[t][4 * jj + 2] * scale,
+                           acc[t][4 * jj + 3] * scale));
+  constexpr int LPR = W / 8;                  // lanes per row, 16 bytes each
+  constexpr int RPI = 64 / LPR;               // rows per instruction
+  const int rr = lane / LPR, ch = lane % LPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + rr;
+    const u32x4 v = lds_read16(stage, row * RS + ch * 16);
+    if (row < rows) *reinterpret_cast<u32x4*>(g0 + (size_t)row * row_stride + ch * 8) = v;
+  }
+}
+
 }  // namespace fa

@@ -268,22 +268,15 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
       if (g == 0) p.lse_part[prow] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
     }
   } else {
+    // O rows q0 + 32 wave.. go out through this wave's part of the (now idle) tile buffers
+    static_assert(NW * stage_bytes<D>() <= 4 * TILE, "staging fits the tile buffers");
     const float l_tot = pair_sum(l_run);
-    if (qw < lq) {
-      const float inv = l_tot > 0.f ? (DROP ? p.drop.rescale : 1.f) / l_tot : 0.f;
-      T* __restrict__ Og = reinterpret_cast<T*>(p.o) + hv.q_off + (size_t)qw * hv.q_stride;
-#pragma unroll
-      for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          u32x2 w = pack4<DT>(acc[dt][4 * jj] * inv, acc[dt][4 * jj + 1] * inv,
-                              acc[dt][4 * jj + 2] * inv, acc[dt][4 * jj + 3] * inv);
-          *reinterpret_cast<u32x2*>(Og + 32 * dt + 8 * jj + 4 * g) = w;
-        }
-      if (g == 0) {
-        p.lse[hv.stat_off + (size_t)qw * hv.stat_stride] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
-      }
-    }
+    const float inv = l_tot > 0.f ? (DROP ? p.drop.rescale : 1.f) / l_tot : 0.f;
+    store_tile_rows<DT, D>(acc, inv, smem + wave * stage_bytes<D>(),
+                           reinterpret_cast<T*>(p.o) + hv.q_off + (size_t)(q0 + wave * 32) * hv.q_stride, hv.q_stride,
+                           min(32, lq - (q0 + wave * 32)), lane);
+    if (qw < lq && g == 0)
+      p.lse[hv.stat_off + (size_t)qw * hv.stat_stride] = l_tot > 0.f ? fmaf(m_run, kLn2, __logf(l_tot)) : -INFINITY;
   }
 }
 
