@@ -186,8 +186,8 @@ def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, block_
 
 
 def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = False, block_mask=None,
-             mask_block: int = 128, D=None, stream=None):
-    """Run fa_bwd_preprocess then fa_bwd; returns (dq, dk, dv, D)."""
+             mask_block: int = 128, D=None, stream=None, out=None):
+    """Run fa_bwd_preprocess then fa_bwd; returns (dq, dk, dv, D). `out` = optional (dq, dk, dv)."""
     torch = _torch()
     B, H, N, d = _shape(q)
     if scale is None:
@@ -197,7 +197,7 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
     if D is None:
         D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), B, H, N, d, dt, s), "fa_bwd_preprocess")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
                 float(scale), int(bool(causal)), _ptr(block_mask), mask_block, s)
@@ -220,15 +220,16 @@ def _varlen_shapes(q, k, v, cu_q, cu_k):
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                   scale: Optional[float] = None, causal: bool = False, stream=None):
+                   scale: Optional[float] = None, causal: bool = False, stream=None, out=None, lse=None):
     """fa_fwd_varlen on packed tensors q [total_q, Hq, d], k/v [total_k, Hk, d];
-    returns (o [total_q, Hq, d], lse [total_q, Hq])."""
+    returns (o [total_q, Hq, d], lse [total_q, Hq]) (optionally into `out`, `lse`)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q)
-    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
     st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q),
                        int(max_seqlen_k), hq, hk, d, _dt(q), float(scale), int(bool(causal)), _stream(stream))
@@ -237,8 +238,9 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
 
 
 def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                    scale: Optional[float] = None, causal: bool = False, stream=None):
-    """fa_bwd_preprocess over the packed rows, then fa_bwd_varlen; returns (dq, dk, dv, D)."""
+                    scale: Optional[float] = None, causal: bool = False, stream=None, out=None):
+    """fa_bwd_preprocess over the packed rows, then fa_bwd_varlen; returns (dq, dk, dv, D).
+    `out` = optional (dq, dk, dv)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if scale is None:
@@ -248,7 +250,7 @@ def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     D = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
     if tq > 0:
         _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), 1, hq, tq, d, dt, s), "fa_bwd_preprocess")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
                        cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hk, d,

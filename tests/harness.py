@@ -54,7 +54,9 @@ def mask_dev(mask):
 
 
 def run_gpu(dr: ai.Drawn, scale: float, causal: bool, mask=None, backward: bool = True, poison: bool = True):
-    """fa_fwd (+ fa_bwd_preprocess, fa_bwd) on the drawn inputs. Returns float64 numpy arrays."""
+    """fa_fwd (+ fa_bwd_preprocess, fa_bwd) on the drawn inputs. Returns float64 numpy arrays.
+    With `poison`, every output buffer starts as NaN, so an element a kernel fails to write
+    fails the comparison."""
     import torch
     from exact_io_aware_04_amd import fa
     q, k, v = (to_dev(getattr(dr, n), dr.dtype) for n in "qkv")
@@ -66,7 +68,8 @@ def run_gpu(dr: ai.Drawn, scale: float, causal: bool, mask=None, backward: bool 
     out = {"o_dev": o, "lse_dev": lse}
     if backward:
         do = to_dev(dr.do, dr.dtype)
-        dq, dk, dv, D = fa.backward(q, k, v, o, lse, do, scale, causal, bm)
+        grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v)) if poison else None
+        dq, dk, dv, D = fa.backward(q, k, v, o, lse, do, scale, causal, bm, out=grads)
         out.update(dq=dq, dk=dk, dv=dv, D=D)
     torch.cuda.synchronize()
     res = {"o": from_dev(o, dr.dtype), "lse": lse.double().cpu().numpy()}

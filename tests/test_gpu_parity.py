@@ -171,35 +171,42 @@ def test_backward_is_bitwise_deterministic(causal, d, dtype):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_outputs_stay_inside_their_buffers():
+@pytest.mark.parametrize("n,d,dtype,causal", [(200, 64, ai.F16, True), (300, 128, ai.BF16, False),
+                                              (33, 64, ai.BF16, False), (161, 128, ai.F16, True)])
+def test_outputs_stay_inside_their_buffers(n, d, dtype, causal):
     """Canaries around every output buffer; raw C entry points with sliced pointers."""
     import torch
     from exact_io_aware_04_amd import fa
-    B, H, n, d = 1, 2, 200, 64
-    say("[canary] N=200 d=64 f16 causal")
-    dr = ai.draw(B, H, n, d, ai.F16, 91)
+    B, H = 1, 2
+    say(f"[canary] N={n} d={d} {dtype} causal={causal}")
+    dr = ai.draw(B, H, n, d, dtype, 91 + n + d)
     q, k, v, do = (to_dev(getattr(dr, x), dr.dtype) for x in ("q", "k", "v", "do"))
+    tdt = q.dtype
     numel = B * H * n * d
     PAD = 64
-    def guarded(count, dtype):
-        buf = torch.full((count + 2 * PAD,), 7.0, dtype=dtype, device="cuda")
+    def guarded(count, dt):
+        buf = torch.full((count + 2 * PAD,), 7.0, dtype=dt, device="cuda")
         return buf, buf[PAD:PAD + count]
-    ob, o = guarded(numel, torch.float16)
+    ob, o = guarded(numel, tdt)
     lb, lse = guarded(B * H * n, torch.float32)
     Db, D = guarded(B * H * n, torch.float32)
-    qb_, dq = guarded(numel, torch.float16)
-    kb_, dk = guarded(numel, torch.float16)
-    vb_, dv = guarded(numel, torch.float16)
+    qb_, dq = guarded(numel, tdt)
+    kb_, dk = guarded(numel, tdt)
+    vb_, dv = guarded(numel, tdt)
     s = torch.cuda.current_stream().cuda_stream
+    code = fa.FA_BF16 if dtype == ai.BF16 else fa.FA_F16
+    sc = 1.0 / np.sqrt(d)
     assert fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, n, d,
-                     fa.FA_F16, 0.125, 1, None, 128, s) == 0
-    assert fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), D.data_ptr(), B, H, n, d, fa.FA_F16, s) == 0
+                     code, sc, int(causal), None, 128, s) == 0
+    assert fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), D.data_ptr(), B, H, n, d, code, s) == 0
     assert fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), D.data_ptr(),
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, n, d, fa.FA_F16,
-                     0.125, 1, None, 128, s) == 0
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, n, d, code,
+                     sc, int(causal), None, 128, s) == 0
     torch.cuda.synchronize()
     for buf in (ob, lb, Db, qb_, kb_, vb_):
         assert (buf[:PAD] == 7.0).all() and (buf[-PAD:] == 7.0).all()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t).all()
 
 
 # ---------------------------------------------------------------------------

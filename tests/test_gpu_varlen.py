@@ -36,8 +36,12 @@ def run_varlen(pk: ai.PackedDrawn, hq, hk, scale, causal):
     cu_q, cu_k = _dev_i32(pk.cu_q), _dev_i32(pk.cu_k)
     mq = int(max(1, np.diff(pk.cu_q).max()))
     mk = int(max(1, np.diff(pk.cu_k).max()))
-    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal)
-    dq, dk, dv, D = fa.backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, scale, causal)
+    # outputs start as NaN: an element a kernel fails to write fails the comparison
+    nan = lambda t: torch.full_like(t, float("nan"))
+    lse0 = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device)
+    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal, out=nan(q), lse=lse0)
+    dq, dk, dv, D = fa.backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, scale, causal,
+                                       out=(nan(q), nan(k), nan(v)))
     torch.cuda.synchronize()
     return {"o": from_dev(o, pk.dtype), "lse": lse.double().cpu().numpy(), "dq": from_dev(dq, pk.dtype),
             "dk": from_dev(dk, pk.dtype), "dv": from_dev(dv, pk.dtype), "D": D.double().cpu().numpy(),
@@ -215,3 +219,43 @@ def test_decode_bench_workload_sampled():
         err = float(np.abs(og[sq:eq] - o_ref).max())
         assert err <= O_TOL[w.dtype], f"seq {b}: O error {err:.3e}"
         assert float(np.abs(lg[sq:eq] - lse_ref).max()) <= LSE_TOL, f"seq {b}: LSE"
+
+
+@pytest.mark.parametrize("d,dtype,causal", [(64, ai.F16, True), (128, ai.BF16, False)])
+def test_packed_outputs_stay_inside_their_buffers(d, dtype, causal):
+    """Canaries around every packed output buffer (raw C entry points, sliced
+    pointers); lengths leave ragged row tiles at every sequence end."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    lq, lk, hq, hk = [5, 40, 130], [9, 40, 100], 4, 2
+    say(f"[canary-packed] d={d} {dtype} causal={causal}")
+    pk = ai.draw_packed(lq, lk, hq, hk, d, dtype, 4242 + d)
+    q, k, v, do = (to_dev(getattr(pk, n), pk.dtype) for n in ("q", "k", "v", "do"))
+    cu_q, cu_k = _dev_i32(pk.cu_q), _dev_i32(pk.cu_k)
+    tq, tk = q.shape[0], k.shape[0]
+    PAD = 64
+    def guarded(like_numel, dt):
+        buf = torch.full((like_numel + 2 * PAD,), 7.0, dtype=dt, device="cuda")
+        return buf, buf[PAD:PAD + like_numel]
+    ob, o = guarded(q.numel(), q.dtype)
+    lb, lse = guarded(tq * hq, torch.float32)
+    Db, D = guarded(tq * hq, torch.float32)
+    qb_, dq = guarded(q.numel(), q.dtype)
+    kb_, dk = guarded(k.numel(), k.dtype)
+    vb_, dv = guarded(v.numel(), v.dtype)
+    s = torch.cuda.current_stream().cuda_stream
+    code = fa.FA_BF16 if dtype == ai.BF16 else fa.FA_F16
+    sc = 1.0 / np.sqrt(d)
+    mq, mk = max(lq), max(lk)
+    assert fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            cu_q.data_ptr(), cu_k.data_ptr(), len(lq), tq, tk, mq, mk, hq, hk, d, code, sc,
+                            int(causal), s) == 0
+    assert fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), D.data_ptr(), 1, hq, tq, d, code, s) == 0
+    assert fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), D.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(),
+                            len(lq), tq, tk, mq, mk, hq, hk, d, code, sc, int(causal), s) == 0
+    torch.cuda.synchronize()
+    for buf in (ob, lb, Db, qb_, kb_, vb_):
+        assert (buf[:PAD] == 7.0).all() and (buf[-PAD:] == 7.0).all()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t).all()
