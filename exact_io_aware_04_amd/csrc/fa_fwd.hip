@@ -57,9 +57,11 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
   constexpr int KC = D / 16;                  // contraction chunks over d
   constexpr int NS = BN / 32;                 // 32-key sub-tiles per tile
   constexpr int DT32 = D / 32;
-  static_assert(128 % BM == 0 && 128 % BN == 0, "block-mask granularity");
-
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];
+  // a 256-row block (NW = 8) spans two block-mask rows: launched only without a mask
+  static_assert((128 % BM == 0 || BM == 256) && 128 % BN == 0, "block-mask granularity");
+  // two K/V tile buffers; the epilogue's output staging reuses them
+  constexpr int SMEM = 4 * TILE > NW * stage_bytes<D>() ? 4 * TILE : NW * stage_bytes<D>();
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
     }
   } else {
     // O rows q0 + 32 wave.. go out through this wave's part of the (now idle) tile buffers
-    static_assert(NW * stage_bytes<D>() <= 4 * TILE, "staging fits the tile buffers");
+    static_assert(NW * stage_bytes<D>() <= SMEM, "staging fits the shared buffer");
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? (DROP ? p.drop.rescale : 1.f) / l_tot : 0.f;
     store_tile_rows<DT, D>(acc, inv, smem + wave * stage_bytes<D>(),
@@ -286,10 +288,13 @@ static hipError_t launch_fwd_t(const FwdParams& p0, hipStream_t st) {
   constexpr int BM = NW * 32;
   p.q_blocks = (p.N + BM - 1) / BM;
   p.total_blocks = p.B * p.H * p.q_blocks;
-  if (p.drop.on)
-    hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
-  else
-    hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+  if constexpr (NW == 4) {
+    if (p.drop.on) {
+      hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, true>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<DT, D, BN, NW, false, false>), dim3(p.total_blocks), dim3(NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -359,6 +364,11 @@ hipError_t launch_fwd_splitkv(const FwdParams& p, int is_bf16, hipStream_t st) {
 
 hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
+    // d = 64 without causal masking, block mask or dropout: 8-wave workgroups (256 query
+    // rows) share each K/V tile, halving the tile copies per product (with causal masking
+    // the coarser diagonal costs more than that saves)
+    if (!p.causal && p.mask == nullptr && !p.drop.on)
+      return is_bf16 ? launch_fwd_t<BF16, 64, 64, 8>(p, st) : launch_fwd_t<F16, 64, 64, 8>(p, st);
     return is_bf16 ? launch_fwd_t<BF16, 64, 64, 4>(p, st) : launch_fwd_t<F16, 64, 64, 4>(p, st);
   }
   return is_bf16 ? launch_fwd_t<BF16, 128, 64, 4>(p, st) : launch_fwd_t<F16, 128, 64, 4>(p, st);
