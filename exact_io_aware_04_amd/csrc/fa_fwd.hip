@@ -166,9 +166,20 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
   __syncthreads();
   int buf = 0;
 
+  // a wave with no row of its sequence (split-KV decode: G * n_q rows of 128) only
+  // takes its part in the copies and barriers
+  const bool wave_live = q0 + __builtin_amdgcn_readfirstlane(wave) * 32 < nrows;
+
   while (j < j_end) {
     const int jn = next_kept(j + 1);
     if (jn < j_end) gload(jn, buf ^ 1);     // that buffer was last read before the previous barrier
+    if (!wave_live) {
+      wait_tile_copies();
+      __syncthreads();
+      buf ^= 1;
+      j = jn;
+      continue;
+    }
 
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
