@@ -97,10 +97,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* dO,
  *   O = (P o Z) V with Z = M / (1 - p_drop), M the keep mask, P the softmax
  *   probabilities; lse is that of the scores (dropout acts after the softmax),
  *   so fa_bwd_preprocess applies unchanged (D_i = dO_i . O_i still holds).
- *   Mask: element (head bh = b*H + h, query i, key j) is dropped iff word
- *   j % 4 of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
- *   (j / 4, i, bh, offset) and key (seed mod 2^32, seed / 2^32) is below
- *   floor(p_drop * 2^32). The same (p_drop, seed, offset) must be passed to
+ *   Mask: one Philox4x32-10 call (Salmon, Moraes, Dror, Shaw, SC 2011) with
+ *   counter (j / 4, i / 2, bh, offset) and key (seed mod 2^32, seed / 2^32)
+ *   decides the 2 x 4 block of queries i, keys j it covers: element (head
+ *   bh = b*H + h, query i, key j) is dropped iff the 16-bit half i % 2 (0 =
+ *   low) of word j % 4 is below floor(p_drop * 2^16), so the dropped fraction
+ *   is within 2^-16 of p_drop. The same (p_drop, seed, offset) must be passed to
  *   the forward and the backward; `offset` separates independent masks drawn
  *   with one seed. Otherwise identical to fa_fwd / fa_bwd (dense layout,
  *   causal, block mask). FA_ERR_DROPOUT unless 0 <= p_drop < 1; p_drop = 0

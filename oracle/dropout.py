@@ -19,10 +19,13 @@ numbers: as easy as 1, 2, 3", SC 2011): a 128-bit counter (c0..c3) and a
   (hi0, lo0) = 0xD2511F53 * c0,  (hi1, lo1) = 0xCD9E8D57 * c2  (32 x 32 -> 64 bits),
   (c0, c1, c2, c3) <- (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0),
 with the key advanced by (0x9E3779B9, 0xBB67AE85) between rounds.
-Reading (the pages fix no layout): element (head bh, query i, key j) uses
-word j mod 4 of Philox(counter = (j div 4, i, bh, offset), key = (seed mod
-2^32, seed div 2^32)); it is dropped iff that word < floor(p 2^32) (integer
-comparison, so the decision is exact on both sides). For a packed batch,
+Reading (the pages fix no layout): one generator call decides a block of
+2 queries x 4 keys. Element (head bh, query i, key j) uses the 16-bit half
+i mod 2 (0 = low) of word j mod 4 of Philox(counter = (j div 4, i div 2, bh,
+offset), key = (seed mod 2^32, seed div 2^32)); it is dropped iff that half
+< floor(p 2^16) (integer comparison, so the decision is exact on both sides).
+The kept fraction is 1 - floor(p 2^16) / 2^16, within 2^-16 of 1 - p; the
+rescale stays 1 / (1 - p) as the method states. For a packed batch,
 bh = b H + h and i, j are positions inside sequence b.
 The generator's bit pattern is "parity unpinned": no published output is
 reproduced here; its pins are statistical (keep rate, uniformity, counter
@@ -58,9 +61,9 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def drop_threshold(p: float) -> int:
-    """floor(p 2^32), the integer below which a word means 'dropped'."""
+    """floor(p 2^16), the integer below which a 16-bit draw means 'dropped'."""
     assert 0.0 <= p < 1.0
-    return min(int(np.floor(p * 4294967296.0)), 0xFFFFFFFF)
+    return min(int(np.floor(p * 65536.0)), 0xFFFF)
 
 
 def keep_mask(bh: int, rows, cols, p: float, seed: int, offset: int = 0) -> np.ndarray:
@@ -70,9 +73,11 @@ def keep_mask(bh: int, rows, cols, p: float, seed: int, offset: int = 0) -> np.n
     t = np.uint32(drop_threshold(p))
     i = rows[:, None]
     j = cols[None, :]
-    words = philox4x32_10(j >> 2, i, np.int64(bh), np.int64(offset), seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    words = philox4x32_10(j >> 2, i >> 1, np.int64(bh), np.int64(offset), seed & 0xFFFFFFFF,
+                          (seed >> 32) & 0xFFFFFFFF)
     w = np.choose((j & 3) + np.zeros_like(i), words)
-    return w >= t
+    half = (w >> (np.uint32(16) * (i & 1).astype(np.uint32))) & np.uint32(0xFFFF)
+    return half >= t
 
 
 def forward_head(q, k, v, scale, causal, p, seed, offset, bh, block_mask=None, mask_block=128, diag_offset=0):

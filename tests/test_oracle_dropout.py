@@ -101,3 +101,17 @@ def test_unbiased_over_seeds():
     np.testing.assert_allclose(mean, o0, atol=0.06)
     wrong = np.mean([od.forward_head(q, k, v, 0.7, False, 0.4, s, 0, 0)[0] * 0.6 for s in range(3000)], axis=0)
     assert np.abs(wrong - o0).max() > 0.1    # dropping the rescale is caught
+
+
+def test_queries_sharing_a_call_are_independent():
+    """The two queries of a generator row pair use the two 16-bit halves of the
+    same words; their keep decisions must still be independent."""
+    m = od.keep_mask(4, np.arange(512), np.arange(256), 0.5, 31337, 2)
+    even, odd = m[0::2], m[1::2]
+    n = even.size
+    agree = int((even == odd).sum())
+    assert abs(agree - n / 2) <= 5 * np.sqrt(n / 4)
+    # and the rate of the quantised threshold: floor(p 2^16) / 2^16 dropped
+    p = 0.3
+    t = od.drop_threshold(p)
+    assert t == int(np.floor(p * 65536)) and 0 <= p * 65536 - t < 1
