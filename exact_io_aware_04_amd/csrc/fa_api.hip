@@ -54,13 +54,13 @@ fa_status check_varlen(int batch, int total_q, int total_k, int max_q, int max_k
   return FA_OK;
 }
 
-// Dropout parameters: p in [0, 1) (finite); the drop decision compares a
-// generator word with floor(p 2^32) and kept values are scaled by 1 / (1 - p).
+// Dropout parameters: p in [0, 1) (finite); the drop decision compares a 16-bit
+// generator draw with floor(p 2^16) and kept values are scaled by 1 / (1 - p).
 fa_status make_dropout(float p_drop, uint64_t seed, uint32_t offset, fa::Dropout* d) {
   if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_DROPOUT;
   d->on = 1;
-  const double t = floor((double)p_drop * 4294967296.0);
-  d->threshold = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  const double t = floor((double)p_drop * 65536.0);
+  d->threshold = t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
   d->rescale = (float)(1.0 / (1.0 - (double)p_drop));
   d->seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   d->seed_hi = (uint32_t)(seed >> 32);

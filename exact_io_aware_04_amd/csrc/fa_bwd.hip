@@ -763,12 +763,10 @@ __global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_ker
         }
       }
       if constexpr (DROP) {                   // dP = Z o (dO V^T), Z = M / (1 - p)
+        // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u (as in the forward)
+        const uint32_t kb16 = keep16_pair(p.drop, (uint32_t)((k0 + 32 * t) >> 2), (uint32_t)qw, (uint32_t)bh, lane);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t kb4 = keep4(p.drop, (uint32_t)((k0 + 32 * t + 8 * jj + 4 * g) >> 2), (uint32_t)qw, (uint32_t)bh);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) dp[4 * jj + u] = ((kb4 >> u) & 1) ? dp[4 * jj + u] * p.drop.rescale : 0.f;
-        }
+        for (int r = 0; r < 16; ++r) dp[r] = ((kb16 >> r) & 1) ? dp[r] * p.drop.rescale : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) de[r] *= dp[r] - dq_d;

@@ -314,31 +314,61 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   }
   return u32x4{c0, c1, c2, c3};
 }
-// Keep bits of elements (bh, i, 4 c .. 4 c + 3): bit u set iff word u >= threshold.
-__device__ __forceinline__ uint32_t keep4(const Dropout& dr, uint32_t c, uint32_t i, uint32_t bh) {
-  const u32x4 w = philox4x32_10(c, i, bh, dr.offset, dr.seed_lo, dr.seed_hi);
-  return (uint32_t)(w[0] >= dr.threshold) | ((uint32_t)(w[1] >= dr.threshold) << 1) |
-         ((uint32_t)(w[2] >= dr.threshold) << 2) | ((uint32_t)(w[3] >= dr.threshold) << 3);
+// One generator call decides a block of 2 queries x 4 keys: element (query
+// 2 r + h, key 4 c + u) of head bh is kept iff the 16-bit half h (0 = low) of
+// word u is >= threshold (= floor(p 2^16)). Returns the eight keep bits, bit
+// 4 h + u.
+__device__ __forceinline__ uint32_t keep8(const Dropout& dr, uint32_t c, uint32_t r, uint32_t bh) {
+  const u32x4 w = philox4x32_10(c, r, bh, dr.offset, dr.seed_lo, dr.seed_hi);
+  uint32_t b = 0u;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    b |= (uint32_t)((w[u] & 0xFFFFu) >= dr.threshold) << u;
+    b |= (uint32_t)((w[u] >> 16) >= dr.threshold) << (4 + u);
+  }
+  return b;
 }
 
-// Keep bits of the 16 elements a lane holds in a key-per-lane accumulator:
-// column (key) 4 c + (lane & 3), rows i0 + 8 j + v for j, v in 0..3, as bit
-// 4 j + v. The four lanes of a quad hold keys 4 c .. 4 c + 3, which one
-// generator call covers, so each lane makes the call for row i0 + 8 j +
-// (lane & 3) and the quad exchanges the four keep bits of each call.
+// Keep bits of the 16 elements a lane holds in a query-per-lane accumulator
+// (forward, dQ): query i (i mod 2 = lane mod 2), keys 4 (c0 + 2 j + g) + u for
+// j, u in 0..3 (g = lane / 32), as bit 4 j + u. Lanes 2a and 2a + 1 hold the two
+// queries of one generator row pair: each draws two of the four blocks (j = its
+// parity and j + 2) and the pair swaps the nibbles that belong to the other query.
+__device__ __forceinline__ uint32_t keep16_pair(const Dropout& dr, uint32_t c0, uint32_t i, uint32_t bh, int lane) {
+  const uint32_t odd = (uint32_t)lane & 1u, g = ((uint32_t)lane >> 5) & 1u;
+  const uint32_t b0 = keep8(dr, c0 + 2u * odd + g, i >> 1, bh);        // block j = odd
+  const uint32_t b1 = keep8(dr, c0 + 2u * (odd + 2u) + g, i >> 1, bh); // block j = odd + 2
+  const uint32_t sh = 4u * odd;
+  const uint32_t own = ((b0 >> sh) & 0xFu) | (((b1 >> sh) & 0xFu) << 4);
+  const uint32_t give = ((b0 >> (4u - sh)) & 0xFu) | (((b1 >> (4u - sh)) & 0xFu) << 4);
+  // quad_perm [1, 0, 3, 2]: the partner's nibbles of this lane's query, blocks j = 1 - odd, 3 - odd
+  const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
+  const uint32_t even_j = odd ? got : own;    // blocks j = 0, 2
+  const uint32_t odd_j = odd ? own : got;     // blocks j = 1, 3
+  return (even_j & 0xFu) | ((odd_j & 0xFu) << 4) | ((even_j & 0xF0u) << 4) | ((odd_j & 0xF0u) << 8);
+}
+
+// Keep bits of the 16 elements a lane holds in a key-per-lane accumulator
+// (dK/dV): key 4 c + (lane & 3), queries i0 + 8 j + v for j, v in 0..3 (i0
+// even), as bit 4 j + v. The quad's four keys share one call per row pair
+// (i0 + 8 j + 2 s, + 1), P = 2 j + s; quad lane P mod 4 draws pair P (its
+// calls P = lane & 3 and P + 4) and the quad broadcasts the eight bits.
 template <int V>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, V * 0x55, 0xF, 0xF, false);
 }
 __device__ __forceinline__ uint32_t keep16_quad(const Dropout& dr, uint32_t c, uint32_t i0, uint32_t bh, int lane) {
-  const uint32_t u = (uint32_t)lane & 3u;
+  const uint32_t v = (uint32_t)lane & 3u;
+  const uint32_t r0 = (i0 + 8u * (v >> 1) + 2u * (v & 1u)) >> 1;    // pair P = v
+  const uint32_t x = keep8(dr, c, r0, bh) | (keep8(dr, c, r0 + 8u, bh) << 8);  // and P + 4 (rows + 16)
+  const uint32_t xs[4] = {quad_bcast<0>(x), quad_bcast<1>(x), quad_bcast<2>(x), quad_bcast<3>(x)};
   uint32_t kmask = 0u;
-#pragma unroll 1
-  for (int j = 0; j < 4; ++j) {              // rolled: one generator call live at a time
-    const uint32_t b = keep4(dr, c, i0 + 8u * (uint32_t)j + u, bh);
-    const uint32_t row4 = ((quad_bcast<0>(b) >> u) & 1u) | (((quad_bcast<1>(b) >> u) & 1u) << 1) |
-                          (((quad_bcast<2>(b) >> u) & 1u) << 2) | (((quad_bcast<3>(b) >> u) & 1u) << 3);
-    kmask |= row4 << (4 * j);
+#pragma unroll
+  for (int P = 0; P < 8; ++P) {
+    const uint32_t byte = (xs[P & 3] >> (8 * (P >> 2))) & 0xFFu;
+    const int r = 4 * (P >> 1) + 2 * (P & 1);  // register of row i0 + 8 j + 2 s
+    kmask |= ((byte >> v) & 1u) << r;
+    kmask |= ((byte >> (4u + v)) & 1u) << (r + 1);
   }
   return kmask;
 }

@@ -234,13 +234,11 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
       l_run = sum8<DT>(pb[t][0], l_run);
       l_run = sum8<DT>(pb[t][1], l_run);
       if constexpr (DROP) {
-        // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u: one generator call per jj
+        // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u: two generator calls
+        // per lane, shared with the lane that holds the other query of the row pair
+        const uint32_t kb16 = keep16_pair(p.drop, (uint32_t)((k0 + 32 * t) >> 2), (uint32_t)qw, (uint32_t)bh, lane);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t kb4 = keep4(p.drop, (uint32_t)((k0 + 32 * t + 8 * jj + 4 * g) >> 2), (uint32_t)qw, (uint32_t)bh);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) e[4 * jj + u] = ((kb4 >> u) & 1) ? e[4 * jj + u] : 0.f;
-        }
+        for (int r = 0; r < 16; ++r) e[r] = ((kb16 >> r) & 1) ? e[r] : 0.f;
         pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
         pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
       }
