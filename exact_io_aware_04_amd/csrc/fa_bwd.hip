@@ -635,10 +635,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per block of NW*32 queries, looping over key tiles
 // ---------------------------------------------------------------------------
-// Register target: three waves per SIMD (<= 168 VGPRs) at d = 64 without
-// dropout, two otherwise.
+// Register target: three waves per SIMD (<= 168 VGPRs) at d = 64 (with or
+// without dropout), two at d = 128.
 template <int D, bool DROP>
-struct DqOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 3 : 2; };
+struct DqOccupancy { static constexpr int value = D <= 64 ? 3 : 2; };
 
 template <class DT, int D, int BN, int NW, bool DROP>
 __global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_kernel(BwdParams p) {
