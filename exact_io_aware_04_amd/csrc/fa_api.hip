@@ -40,15 +40,17 @@ fa_status check_mask(const uint8_t* m, int mb) { return (m != nullptr && mb != 1
 
 // Packed variable-length batches: byte offsets inside one (sequence, head) are
 // 32-bit (rows up to max_seqlen, heads x d elements apart), and the dispatch
-// grids (query blocks of 128 x 256 threads, key blocks of 128 x 512 threads)
-// count work-items in 32 bits.
+// grids (query blocks of 128 x 256 threads or, for the d = 64 forward without
+// causal masking, 256 x 512 threads; key blocks of 128 x 512 threads) count
+// work-items in 32 bits.
 fa_status check_varlen(int batch, int total_q, int total_k, int max_q, int max_k, int Hq, int Hk, int d) {
   if (batch < 1 || total_q < 0 || total_k < 0 || max_q < 1 || max_k < 1 || Hq < 1 || Hk < 1) return FA_ERR_SHAPE;
   if (Hq % Hk != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if ((long long)max_q * Hq * d * 2 >= (1LL << 31) || (long long)max_k * Hk * d * 2 >= (1LL << 31)) return FA_ERR_SHAPE;
   if ((long long)max_q * Hq * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
-  const long double qg = (long double)batch * Hq * ((max_q + 127) / 128) * 256.0L;
+  const long double qg = (long double)batch * Hq *
+                         fmaxl(((max_q + 127) / 128) * 256.0L, ((max_q + 255) / 256) * 512.0L);
   const long double kg = (long double)batch * Hk * ((max_k + 127) / 128) * 512.0L;
   if (qg > 4.0e9L || kg > 4.0e9L) return FA_ERR_SHAPE;
   return FA_OK;

@@ -131,6 +131,9 @@ VARLEN_CASES = [
     (dict(q=None), -1), (dict(cu_q=None), -1), (dict(cu_k=None), -1),
     (dict(batch=0), -2), (dict(total_q=-1), -2), (dict(max_q=0), -2), (dict(max_k=0), -2),
     (dict(Hq=3, Hk=2), -2), (dict(Hk=0), -2), (dict(max_q=1 << 20, Hq=64), -2), (dict(max_k=1 << 20, Hk=64), -2),
+    # many one-token sequences with grouped heads: the 8-wave forward grid (256-row
+    # blocks of 512 threads) would pass 2^32 work-items although 128-row blocks would not
+    (dict(batch=1_500_000, total_q=1_500_000, total_k=1_500_000, max_q=1, max_k=1, Hq=8, Hk=1), -2),
     (dict(dt=3), -3), (dict(d=96), -4),
     (dict(o=MIS), -6), (dict(scale=0.0), -8),
 ]
