@@ -167,14 +167,44 @@ def _shape(q):
     return tuple(int(x) for x in q.shape)
 
 
+def _expect(t, shape, dtype, like, name: str):
+    """Every buffer handed to the library must be contiguous, of the given shape and
+    dtype, and on q's device: the C entry points only see pointers and sizes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != like.device:
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} on {like.device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _expect_mask(block_mask, N: int, mask_block: int, like):
+    if block_mask is None:
+        return
+    t = -(-N // mask_block) if mask_block > 0 else 0
+    _expect(block_mask, (t, t), _torch().uint8, like, "block_mask")
+
+
+def _dense_args(q, k, v, block_mask, mask_block, **others):
+    """Shape checks of the dense entry points; `others` maps names to (tensor, kind)
+    with kind 'qkv' ([B, H, N, d], q's dtype) or 'row' ([B, H, N] float32)."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    _expect(k, q.shape, q.dtype, q, "k")
+    _expect(v, q.shape, q.dtype, q, "v")
+    for name, (t, kind) in others.items():
+        if kind == "qkv":
+            _expect(t, q.shape, q.dtype, q, name)
+        else:
+            _expect(t, (B, H, N), torch.float32, q, name)
+    _expect_mask(block_mask, N, mask_block, q)
+    return B, H, N, d
+
+
 def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, block_mask=None,
             mask_block: int = 128, out=None, lse=None, stream=None):
     """Run fa_fwd on [B, H, N, d] torch tensors; returns (o, lse)."""
     torch = _torch()
-    B, H, N, d = _shape(q)
-    for t in (k, v):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and be contiguous")
+    B, H, N, d = _dense_args(q, k, v, block_mask, mask_block, out=(out, "qkv"), lse=(lse, "row"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
@@ -189,7 +219,9 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
              mask_block: int = 128, D=None, stream=None, out=None):
     """Run fa_bwd_preprocess then fa_bwd; returns (dq, dk, dv, D). `out` = optional (dq, dk, dv)."""
     torch = _torch()
-    B, H, N, d = _shape(q)
+    grads = out if out is not None else (None, None, None)
+    B, H, N, d = _dense_args(q, k, v, block_mask, mask_block, o=(o, "qkv"), dO=(dO, "qkv"), lse=(lse, "row"),
+                             D=(D, "row"), dq=(grads[0], "qkv"), dk=(grads[1], "qkv"), dv=(grads[2], "qkv"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = _dt(q)
@@ -225,6 +257,8 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     returns (o [total_q, Hq, d], lse [total_q, Hq]) (optionally into `out`, `lse`)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _expect(out, q.shape, q.dtype, q, "out")
+    _expect(lse, (tq, hq), torch.float32, q, "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = out if out is not None else torch.empty_like(q)
@@ -243,6 +277,10 @@ def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     `out` = optional (dq, dk, dv)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    grads = out if out is not None else (None, None, None)
+    for name, t, like in (("o", o, q), ("dO", dO, q), ("dq", grads[0], q), ("dk", grads[1], k), ("dv", grads[2], v)):
+        _expect(t, like.shape, q.dtype, q, name)
+    _expect(lse, (tq, hq), torch.float32, q, "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = _dt(q)
@@ -276,6 +314,8 @@ def forward_splitkv(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     o = torch.empty_like(q)
     lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
     opart, lpart = splitkv_workspace(tq, hq, d, n_splits, q.device) if workspace is None else workspace
+    _expect(opart, (n_splits, tq, hq, d), torch.float32, q, "workspace[0]")
+    _expect(lpart, (n_splits, tq, hq), torch.float32, q, "workspace[1]")
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q),
                         int(max_seqlen_k), hq, hk, d, _dt(q), float(scale), int(bool(causal)), int(n_splits),
@@ -288,7 +328,7 @@ def forward_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, scale: O
                     causal: bool = False, block_mask=None, mask_block: int = 128, stream=None):
     """fa_fwd_dropout on [B, H, N, d] tensors; returns (o, lse)."""
     torch = _torch()
-    B, H, N, d = _shape(q)
+    B, H, N, d = _dense_args(q, k, v, block_mask, mask_block)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
@@ -304,7 +344,7 @@ def backward_dropout(q, k, v, o, lse, dO, p_drop: float, seed: int, offset: int 
                      causal: bool = False, block_mask=None, mask_block: int = 128, stream=None):
     """fa_bwd_preprocess then fa_bwd_dropout (same p_drop, seed, offset as the forward); returns (dq, dk, dv, D)."""
     torch = _torch()
-    B, H, N, d = _shape(q)
+    B, H, N, d = _dense_args(q, k, v, block_mask, mask_block, o=(o, "qkv"), dO=(dO, "qkv"), lse=(lse, "row"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = _dt(q)

@@ -187,3 +187,28 @@ def test_binding_keeps_a_single_hip_runtime():
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split() == ["1", "1"], out.stdout
+
+
+def test_binding_rejects_mismatched_buffers():
+    """The torch wrappers check every buffer they hand to the C entry points
+    (shape, dtype, contiguity, device) before any HIP call."""
+    import torch
+    q = torch.zeros((1, 2, 64, 64), dtype=torch.float16)
+    k, v, o, do = (torch.zeros_like(q) for _ in range(4))
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32)
+    bad = [
+        lambda: fa.forward(q, k[:, :, :32], v),                                   # k shorter than q
+        lambda: fa.forward(q, k, v.to(torch.bfloat16)),                           # dtype mismatch
+        lambda: fa.forward(q, k, v, out=torch.zeros((1, 2, 64, 32), dtype=torch.float16)),
+        lambda: fa.forward(q, k, v, lse=torch.zeros((1, 2, 64), dtype=torch.float16)),
+        lambda: fa.forward(q, k, v, block_mask=torch.ones((2, 2), dtype=torch.uint8)),   # needs 1 x 1
+        lambda: fa.forward(q, k, v.transpose(2, 3)),                              # not contiguous
+        lambda: fa.backward(q, k, v, o, lse, do[:, :1]),
+        lambda: fa.backward(q, k, v, o, lse[:, :, :10], do),
+        lambda: fa.backward(q, k, v, o, lse, do, out=(torch.zeros_like(q), torch.zeros_like(q), q[:, :1])),
+        lambda: fa.forward_dropout(q, k[:, :1], v, 0.1, 1),
+        lambda: fa.backward_dropout(q, k, v, o[:, :, :8], lse, do, 0.1, 1),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
