@@ -292,3 +292,49 @@ def test_full_causal_64k_sampled():
         assert np.linalg.norm(sum_dk) <= 1e-2 * np.abs(res["dk"][0, h]).sum(axis=0).max()
     for n in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[n]).all()
+
+
+def test_largest_head_d128_causal():
+    """The largest head the ABI accepts at d = 128 (N d 4 < 2^31: N = 4,194,303,
+    ragged against every tile size): byte offsets inside the head reach ~1 GiB
+    and the buffer ranges approach 2^31. Sampled rows of O/LSE/dQ and late key
+    columns of dK/dV against the oracle, gradient invariants over the whole head."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    N, d = 4_194_303, 128
+    say(f"[largest] N={N} d={d} bf16 causal: drawing inputs")
+    dr = ai.draw(1, 1, N, d, ai.BF16, 4242)
+    q, k, v, do = (to_dev(getattr(dr, n), dr.dtype) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / np.sqrt(d)
+    say("[largest] GPU forward + backward")
+    o, lse = fa.forward(q, k, v, scale, True)
+    dq, dk, dv, _ = fa.backward(q, k, v, o, lse, do, scale, True)
+    torch.cuda.synchronize()
+    for name, t in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), f"largest head: non-finite {name}"
+    # whole-head invariants (any N): sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
+    sum_dv = dv[0, 0].double().sum(dim=0).cpu().numpy()
+    sum_do = do[0, 0].double().sum(dim=0).cpu().numpy()
+    assert rel_fro(sum_dv, sum_do) <= GRAD_REL_TOL
+    sum_dk = dk[0, 0].double().sum(dim=0).cpu().numpy()
+    assert np.linalg.norm(sum_dk) <= 1e-2 * float(dk[0, 0].double().abs().sum(dim=0).max())
+    rng = np.random.Generator(np.random.PCG64(17))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, N // 2, N - 129, N - 2, N - 1], rng.integers(0, N, 8)]))
+    first = N - 256
+    cols = np.unique(np.concatenate([[N - 1, N - 2, N - 128, N - 129, N - 256], rng.integers(first, N, 11)]))
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = {"o": o[0, 0, ri].float().cpu().numpy().astype(np.float64),
+           "lse": lse[0, 0, ri].double().cpu().numpy(),
+           "dq": dq[0, 0, ri].float().cpu().numpy().astype(np.float64),
+           "dk": dk[0, 0, ci].float().cpu().numpy().astype(np.float64),
+           "dv": dv[0, 0, ci].float().cpu().numpy().astype(np.float64)}
+    del q, k, v, do, o, lse, dq, dk, dv
+    say("[largest] oracle on sampled rows / columns")
+    q64, k64, v64, do64 = (dr.f64(n, 0, 0) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = oracle.forward_head(q64, k64, v64, scale, True, None, 128, rows=rows, row_block=16)
+    check_forward(got["o"], got["lse"], o_ref, lse_ref, ai.BF16, "largest head")
+    gq, gk, gv, _ = oracle.backward_head_sampled(q64, k64, v64, do64, scale, True, None, 128, rows, cols,
+                                                 first_row=first, row_block=16)
+    check_grads({"dq": got["dq"], "dk": got["dk"], "dv": got["dv"]}, {"dq": gq, "dk": gk, "dv": gv},
+                "largest head sampled")
+
