@@ -166,6 +166,21 @@ def draw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return Drawn(dtype, out[0], out[1], out[2], out[3] if with_do else None)
 
 
+def draw_ramped_keys(B: int, H: int, N: int, d: int, dtype: str, seed: int, lo: float, hi: float,
+                     q_mult: float = 1.0) -> Drawn:
+    """Like draw(), but key row j is multiplied by lo + (hi - lo) j / (N - 1) (and q by
+    q_mult) before rounding, so that scores grow along the key axis: each query row's
+    running maximum keeps rising as later key tiles arrive."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    ramp = (lo + (hi - lo) * np.arange(N, dtype=np.float32) / np.float32(max(N - 1, 1))).astype(np.float32)
+    q = rng.standard_normal(shape, dtype=np.float32) * np.float32(q_mult)
+    k = rng.standard_normal(shape, dtype=np.float32) * ramp[None, None, :, None]
+    v = rng.standard_normal(shape, dtype=np.float32)
+    do = rng.standard_normal(shape, dtype=np.float32)
+    return Drawn(dtype, *(round_bits(x, dtype) for x in (q, k, v, do)))
+
+
 def draw_workload(w: Workload, with_do: Optional[bool] = None) -> Drawn:
     if with_do is None:
         with_do = w.backward

@@ -21,7 +21,10 @@ import attn_inputs as ai
 
 O_TOL = {ai.F16: 2e-3, ai.BF16: 1e-2}
 GRAD_REL_TOL = 2e-2
-LSE_TOL = 2e-3
+# LSE: the kernels add the probabilities rounded to the operand type (RNE, unit
+# roundoff u = 2^-11 fp16, 2^-8 bf16) into the row sum l, so |d ln l| <= u; plus
+# fp32 / hardware exp2-log error (~1e-5). fp16 keeps the looser 2e-3.
+LSE_TOL = {ai.F16: 2e-3, ai.BF16: 4e-3}
 
 
 def say(msg: str) -> None:
@@ -93,7 +96,7 @@ def check_forward(o, lse, o_ref, lse_ref, dtype, what=""):
     live = np.isfinite(lse_ref)
     assert (np.isneginf(lse) == ~live).all(), f"{what}: LSE -inf pattern differs"
     lerr = float(np.abs(lse[live] - lse_ref[live]).max()) if live.any() else 0.0
-    assert lerr <= LSE_TOL, f"{what}: LSE max-abs error {lerr:.3e}"
+    assert lerr <= LSE_TOL[dtype], f"{what}: LSE max-abs error {lerr:.3e}"
     return err, lerr
 
 

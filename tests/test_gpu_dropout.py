@@ -52,7 +52,7 @@ def test_dropout_parity(n, d, dtype, mode, p):
         live = np.isfinite(lse_ref)
         assert (np.isneginf(res["lse"][0, h]) == ~live).all(), what
         if live.any():
-            assert float(np.abs(res["lse"][0, h][live] - lse_ref[live]).max()) <= LSE_TOL, what
+            assert float(np.abs(res["lse"][0, h][live] - lse_ref[live]).max()) <= LSE_TOL[dtype], what
         for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
             e = rel_fro(res[name][0, h], ref)
             assert e <= GRAD_REL_TOL, f"{what}: {name} relative error {e:.3e}"

@@ -11,8 +11,8 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from harness import (GRAD_REL_TOL, check_D, check_forward, check_grads, from_dev, rel_fro, run_gpu,
-                     say, to_dev)
+from harness import (GRAD_REL_TOL, LSE_TOL, check_D, check_forward, check_grads, from_dev, rel_fro,
+                     run_gpu, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +55,62 @@ def test_small_shapes(n, d, dtype, mode):
         check_forward(res["o"][0, h], res["lse"][0, h], ref["o"], ref["lse"], dtype, what)
         check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
         check_D(res["D"][0, h], dr.f64("do", 0, h), o_dev[0, h], what)
+
+
+def _rescales_per_row(s_scaled, causal, tile=64, threshold=8.0):
+    """How often the forward's conditional rescale fires per row on these scores:
+    the running reference moves (after the first tile) when a tile's maximum, in
+    log2 units, exceeds it by more than `threshold`. Test-side coverage count only."""
+    n = s_scaled.shape[0]
+    x = s_scaled * np.log2(np.e)
+    if causal:
+        x = np.where(np.tril(np.ones((n, n), dtype=bool)), x, -np.inf)
+    counts = np.zeros(n, dtype=np.int64)
+    ref = np.full(n, -np.inf)
+    for j0 in range(0, n, tile):
+        m = x[:, j0:j0 + tile].max(axis=1)
+        grow = m > ref + threshold
+        counts += grow & np.isfinite(ref)
+        ref = np.where(grow, m, ref)
+    return counts
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [ai.F16, ai.BF16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_running_max_keeps_rising(d, dtype, causal):
+    """Key norms ramp up along the sequence, so every row's maximum climbs tile
+    after tile and the forward rescales its running state several times per
+    row (counted below from the oracle's scores); results must still match."""
+    n = 1000
+    seed = 777 + d + (1 if dtype == ai.BF16 else 0) + (2 if causal else 0)
+    say(f"[rescale] N={n} d={d} {dtype} causal={causal} seed={seed}")
+    dr = ai.draw_ramped_keys(1, 2, n, d, dtype, seed, lo=0.2, hi=12.0, q_mult=2.0)
+    scale = 1.0 / np.sqrt(d)
+    q0, k0 = dr.f64("q", 0, 0), dr.f64("k", 0, 0)
+    fired = _rescales_per_row(scale * (q0 @ k0.T), causal)
+    assert fired[n // 2:].mean() >= 2.0, f"inputs exercise too few rescales ({fired.mean():.2f} per row)"
+    res = run_gpu(dr, scale, causal, None, backward=True)
+    # O bound for a softmax this peaked: the PV product consumes the probabilities
+    # rounded to the operand type (RNE, unit roundoff u), which moves O_ic by at most
+    # u sum_j P_ij |V_jc - O_ic| <= u ((P |V|)_ic + |O_ic|) (the weights stay
+    # normalised), and O itself is rounded (u |O_ic|). A wrong rescale factor errs by O(1).
+    u = 2.0 ** -11 if dtype == ai.F16 else 2.0 ** -8
+    for h in range(2):
+        ref = _oracle_head(dr, 0, h, scale, causal, None)
+        what = f"rescale N={n} d={d} {dtype} causal={causal} h={h}"
+        q, k, v = (dr.f64(x, 0, h) for x in "qkv")
+        sc = scale * (q @ k.T)
+        if causal:
+            sc = np.where(np.tril(np.ones((n, n), dtype=bool)), sc, -np.inf)
+        p = np.exp(sc - ref["lse"][:, None])
+        bound = u * (p @ np.abs(v) + 2.0 * np.abs(ref["o"])) + 1e-4
+        o = res["o"][0, h]
+        assert np.isfinite(o).all(), what
+        assert (np.abs(o - ref["o"]) <= bound).all(), \
+            f"{what}: O error {np.abs(o - ref['o']).max():.3e} beyond the rounding bound"
+        assert np.abs(res["lse"][0, h] - ref["lse"]).max() <= LSE_TOL[dtype], f"{what}: LSE"
+        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -66,3 +66,14 @@ def test_workload_table():
     c5 = w["butterfly_b4_h16_n16384_d64_f16"]
     assert c5.block_mask().shape == (128, 128) and c5.block_mask().sum() == 1024
     assert w["single_head_fwd_n256_d64_f16"].scale == 0.125
+
+
+def test_ramped_keys_are_seeded_and_rise():
+    a = ai.draw_ramped_keys(1, 2, 300, 64, ai.F16, 5, lo=0.2, hi=12.0, q_mult=2.0)
+    b = ai.draw_ramped_keys(1, 2, 300, 64, ai.F16, 5, lo=0.2, hi=12.0, q_mult=2.0)
+    for n in ("q", "k", "v", "do"):
+        np.testing.assert_array_equal(getattr(a, n), getattr(b, n))
+        assert getattr(a, n).shape == (1, 2, 300, 64) and getattr(a, n).dtype == np.uint16
+    k = np.abs(a.f64("k", 0, 1))
+    assert k[-10:].mean() > 20 * k[:10].mean()        # key rows scaled from 0.2 up to 12
+    assert 1.5 < np.abs(a.f64("q")).std() / 0.8 < 3.0  # q scaled by 2 (|N(0,1)| has sd ~0.6)
