@@ -230,13 +230,15 @@ def bench_packed(args, w) -> int:
         achieved = b_fwd / (fwd_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": "fa_fwd_splitkv", "achieved": round(achieved, 1),
                     "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / metrics.MI355X_HBM_GBPS, 4),
-                    "traffic": None, "launch_ms": round(fwd_ms, 4), "bytes_per_launch": b_fwd}
+                    "traffic": measured_traffic(w.name, "fa_fwd_splitkv"), "launch_ms": round(fwd_ms, 4),
+                    "bytes_per_launch": b_fwd}
         metric = "decode forward (split-KV) HBM GB/s and TFLOP/s, packed GQA batch"
     else:
         achieved = f_bwd / (bwd_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": "fa_bwd_varlen", "achieved": round(achieved, 2),
                     "peak": metrics.MI355X_PEAK_DENSE_F16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / metrics.MI355X_PEAK_DENSE_F16_TFLOPS, 4), "traffic": None,
+                    "frac": round(achieved / metrics.MI355X_PEAK_DENSE_F16_TFLOPS, 4),
+                    "traffic": measured_traffic(w.name, "fa_bwd_varlen"),
                     "launch_ms": round(bwd_ms, 4), "flops_per_launch": f_bwd}
         metric = "packed varlen GQA attention fwd+bwd TFLOP/s"
     result = {
