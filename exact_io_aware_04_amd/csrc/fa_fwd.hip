@@ -41,9 +41,9 @@ constexpr float kRescaleThreshold = 8.0f;
 // DROP: dropout on P after the softmax (dense layout, not with SPLIT): the row
 // sum uses the undropped probabilities, the product P V the dropped ones, and
 // the epilogue applies 1 / (1 - p) with the normalisation.
-// Register target: at least three waves per SIMD (<= 168 VGPRs) for d = 64
-// with 64-key tiles unless the dropout generator is inlined (the kernel needs
-// 128, so four run), two for d = 128.
+// Register target (minimum waves per SIMD): three at d = 64 without dropout
+// (<= 168 VGPRs; the kernel fits in 128, so four run), two at d = 64 with the
+// dropout generator inlined (165 VGPRs, so three run) and at d = 128.
 template <int D, bool DROP>
 struct FwdOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 3 : 2; };
 
