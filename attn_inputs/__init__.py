@@ -39,14 +39,18 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     0x7FFF plus the lowest kept bit before truncating rounds halfway cases to
     the even neighbour; overflow past the largest finite value carries into
     the exponent and yields infinity, as IEEE rounding requires. NaNs map to a
-    quiet NaN.
+    quiet NaN. Every non-NaN pattern is at most 0xFF800000 (-inf), so the sum
+    stays within 32 bits.
     """
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (b >> 16) & 1
-    r = ((b + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
-    if nan.any():
-        r = np.where(nan, np.uint16(0x7FC0), r)
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    nan = np.isnan(f)
+    has_nan = bool(nan.any())
+    b = f.view(np.uint32)
+    if has_nan:
+        b = np.where(nan, np.uint32(0), b)
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    if has_nan:
+        r[nan] = np.uint16(0x7FC0)
     return r
 
 

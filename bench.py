@@ -8,11 +8,15 @@ enqueues the three C-ABI calls. Prints ONE JSON line on stdout.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-The default workload is the GPT-2-medium attention shape (batch 64, 16 heads,
-length 1024, head dim 64, fp16, dense). Other workload names come from
-attn_inputs.WORKLOADS, and attn_inputs.PACKED_WORKLOADS (packed variable-length
-batches with grouped key/value heads: forward + backward through
-fa_fwd_varlen / fa_bwd_varlen, or decode through fa_fwd_splitkv).
+The default workload is the largest single-GPU one in the metric's range: causal
+attention over 65536 tokens (batch 1, 8 heads, head dim 128, bf16). The other
+workloads of that range (causal N=8192 d=128, butterfly block-sparse N=16384
+d=64) are timed in the same run and reported under "other_workloads". Other
+workload names come from attn_inputs.WORKLOADS, and attn_inputs.PACKED_WORKLOADS
+(packed variable-length batches with grouped key/value heads: forward +
+backward through fa_fwd_varlen / fa_bwd_varlen, or decode through
+fa_fwd_splitkv). The oracle CPU baseline runs first, on a bounded sample of the
+same workload, in a pool of worker processes.
 """
 from __future__ import annotations
 
@@ -28,7 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd+bwd TFLOP/s and % of MFMA bf16 peak, N=1k..64k, d=64/128"
-DEFAULT_WORKLOAD = "gpt2_medium_b64_h16_n1024_d64_f16"
+DEFAULT_WORKLOAD = "causal_b1_h8_n65536_d128_bf16"
+# the other workloads in the metric's N >= 4096 range, reported beside the default one
+EXTRA_WORKLOADS = ["causal_b2_h32_n8192_d128_bf16", "butterfly_b4_h16_n16384_d64_f16"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["fa_device.h", "fa_fwd.hip", "fa_bwd.hip", "fa_launch.h"]
 
@@ -58,55 +64,88 @@ def measured_traffic(workload: str, kernel: str):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(w, dr, budget_s: float, pdrop: float = 0.0):
-    """Time the float64 oracle on whole heads of the same workload until the
-    budget is used (at least one head); scale to TFLOP/s with the same FLOP
-    convention as the GPU figure."""
+def cpu_pool_size() -> int:
+    """Worker processes for the oracle baseline: the cores this process may run
+    on, at most 16 (one GPU's share of a host)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+_CPU_JOB = None      # (workload, drawn inputs, mask, budget, units, pdrop): set before the pool forks
+
+
+def _cpu_worker_init() -> None:
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _cpu_worker(args):
+    """Run the oracle on this worker's share of the units until the budget is used."""
     import numpy as np
     import oracle
+    import oracle.dropout as od
     from exact_io_aware_04_amd import metrics
-    try:
-        from threadpoolctl import threadpool_info
-    except ImportError:
-        threadpool_info = None
-    mask = w.block_mask()
-    pairs = metrics.kept_pairs_per_head(w.N, w.causal, mask)
-    f_fwd, f_bwd = metrics.flops(1, 1, pairs, w.d)
-    per_head = f_fwd + (f_bwd if w.backward else 0)
-    heads, elapsed = 0, 0.0
+    widx, nworkers = args
+    w, dr, mask, budget, units, pdrop = _CPU_JOB
     t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            q, k, v = (dr.f64(n, b, h) for n in "qkv")
-            if pdrop > 0:
-                import oracle.dropout as od
-                od.forward_head(q, k, v, w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h, mask, 128)
-                if w.backward:
-                    od.backward_head(q, k, v, dr.f64("do", b, h), w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h,
-                                     mask, 128)
-            else:
-                oracle.forward_head(q, k, v, w.scale, w.causal, mask, 128)
-                if w.backward:
-                    oracle.backward_head(q, k, v, dr.f64("do", b, h), w.scale, w.causal, mask, 128)
-            heads += 1
-            elapsed = time.perf_counter() - t0
-            if elapsed >= budget_s:
-                break
-        if elapsed >= budget_s:
+    pairs, done, cached = 0, 0, None
+    for b, h, r0, r1 in units[widx::nworkers]:
+        if time.perf_counter() - t0 >= budget:
             break
-    cores = None
-    if threadpool_info is not None:
-        cores = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"), default=None)
-    if not cores:
-        cores = 1
+        if cached is None or cached[0] != (b, h):
+            cached = ((b, h), tuple(dr.f64(n, b, h) for n in (("q", "k", "v", "do") if w.backward else "qkv")))
+        t = cached[1]
+        rows = np.arange(r0, r1)
+        if pdrop > 0:                          # whole heads (the dropout oracle has no row subsets)
+            od.forward_head(*t[:3], w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h, mask, 128)
+            if w.backward:
+                od.backward_head(*t, w.scale, w.causal, pdrop, 0x5EED, 0, b * w.H + h, mask, 128)
+        else:
+            oracle.forward_head(*t[:3], w.scale, w.causal, mask, 128, rows=rows, row_block=128)
+            if w.backward:
+                oracle.backward_head(*t, w.scale, w.causal, mask, 128, row_block=128, rows=rows)
+        pairs += metrics.kept_pairs_rows(rows, w.N, w.causal, mask)
+        done += 1
+    return pairs, done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, dr, budget_s: float, pdrop: float = 0.0, workers: int = 0):
+    """The float64 oracle on a bounded sample of the same workload, timed on the
+    host's cores: units of (head, block of 128 query rows) in a seeded random
+    order are dealt to a pool of single-threaded worker processes, each
+    computing the forward (and backward) of its rows until the budget is used.
+    TFLOP/s under the same FLOP convention as the GPU figure (kept pairs of the
+    rows done x 4d, + 10d with the backward), over the pool's wall time. Must
+    run before this process touches the GPU: the pool forks."""
+    global _CPU_JOB
+    import multiprocessing as mp
+    import numpy as np
+    mask = w.block_mask()
+    rb = w.N if pdrop > 0 else min(w.N, 128)
+    units = [(b, h, r0, min(w.N, r0 + rb)) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, rb)]
+    order = np.random.Generator(np.random.PCG64(w.seed)).permutation(len(units))
+    units = [units[i] for i in order]
+    nw = workers or cpu_pool_size()
+    _CPU_JOB = (w, dr, mask, budget_s, units, pdrop)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(nw, initializer=_cpu_worker_init) as pool:
+        out = pool.map(_cpu_worker, [(i, nw) for i in range(nw)])
+    wall = time.perf_counter() - t0
+    _CPU_JOB = None
+    pairs = sum(o[0] for o in out)
+    done = sum(o[1] for o in out)
+    per_pair = 4 * w.d + (10 * w.d if w.backward else 0)
+    unit = "whole heads" if pdrop > 0 else "(head, 128-query-row block) units"
     return {
-        "value": round(heads * per_head / elapsed / 1e12, 6),
+        "value": round(pairs * per_pair / wall / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": int(nw),
         "kind": "oracle",
-        "sample": (f"{heads} of {w.B * w.H} heads (b,h in row-major order from (0,0)), "
-                   f"{'forward+backward' if w.backward else 'forward'}, float64 numpy oracle "
-                   f"materialising S and P, {elapsed:.1f} s"),
+        "sample": (f"{done} of {len(units)} {unit} of {w.name} in seeded random order, "
+                   f"{'forward+backward' if w.backward else 'forward'}, float64 numpy oracle materialising "
+                   f"S and P rows, {nw} worker processes with one BLAS thread each, {wall:.1f} s wall"),
     }
 
 
@@ -262,41 +301,22 @@ def bench_packed(args, w) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--dropout", type=float, default=0.0,
-                    help="dropout probability on P for dense workloads (fa_fwd_dropout / fa_bwd_dropout); 0 = off")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="time budget of the oracle CPU baseline (0 disables it)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
-              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
-        return 2
-
+def run_dense(w, dr, steps: int, warmup: int, pdrop: float = 0.0):
+    """Time `steps` forward + backward steps of a dense workload on cuda:0.
+    Returns the per-workload figures (throughput, phases, roofline, memory)."""
     import numpy as np
     import torch
     import attn_inputs as ai
     from exact_io_aware_04_amd import fa, metrics
 
-    if args.workload in ai.PACKED_WORKLOADS:
-        return bench_packed(args, ai.PACKED_WORKLOADS[args.workload])
-    if args.workload not in ai.WORKLOADS:
-        log(f"unknown workload {args.workload}; choose from {list(ai.WORKLOADS) + list(ai.PACKED_WORKLOADS)}")
-        return 2
-    w = ai.WORKLOADS[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d
     dt = fa.FA_F16 if w.dtype == ai.F16 else fa.FA_BF16
     tdt = torch.float16 if w.dtype == ai.F16 else torch.bfloat16
     dev = torch.device("cuda:0")
-
-    log(f"[bench] drawing {w.name}")
-    dr = ai.draw_workload(w)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
@@ -306,17 +326,18 @@ def main() -> int:
     mask = w.block_mask()
     bm = torch.from_numpy(mask).to(dev) if mask is not None else None
     o = torch.empty_like(q)
+    io = [q, k, v, o] + ([do] if w.backward else []) + ([bm] if bm is not None else [])
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     if w.backward:
         Dv = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        io += [dq, dk, dv]
     stream = torch.cuda.current_stream(dev)
     s = stream.cuda_stream
     bmp = bm.data_ptr() if bm is not None else None
     causal = int(w.causal)
     scale = float(w.scale)
-
-    pdrop, dseed = float(args.dropout), 0x5EED
+    dseed = 0x5EED
 
     def fwd():
         if pdrop > 0:
@@ -337,17 +358,19 @@ def main() -> int:
                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, scale,
                          causal, bmp, 128, s)
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    torch.cuda.synchronize()
+    free_before = torch.cuda.mem_get_info(dev)[0]
+    log(f"[bench] {w.name}: warmup {warmup}")
+    for _ in range(warmup):
         assert fwd() == 0
         if w.backward:
             assert bwd_pre() == 0
             assert bwd() == 0
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    log(f"[bench] timing {K} steps")
+    log(f"[bench] {w.name}: timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -362,6 +385,7 @@ def main() -> int:
         e[3].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    free_after = torch.cuda.mem_get_info(dev)[0]
     ms_step = (t1 - t0) * 1e3 / K
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     if w.backward:
@@ -377,7 +401,6 @@ def main() -> int:
     peak = metrics.MI355X_PEAK_DENSE_F16_TFLOPS
     fwd_tf = f_fwd / (fwd_ms * 1e-3) / 1e12
     bwd_tf = f_bwd / ((pre_ms + bwd_ms) * 1e-3) / 1e12 if w.backward else None
-
     if w.backward:
         kern, kflops, kms = "fa_bwd", f_bwd, bwd_ms
     else:
@@ -396,34 +419,105 @@ def main() -> int:
     }
     a_fwd, a_bwd = metrics.algorithmic_bytes(B, H, N, d)
     s_fwd, s_all = metrics.standard_attention_bytes(B, H, N)
-
-    result = {
-        "metric": METRIC,
+    io_bytes = sum(t.numel() * t.element_size() for t in io)
+    peak_alloc = torch.cuda.max_memory_allocated(dev) - base_alloc
+    memory = {
+        # device memory beyond the inputs and outputs, at the allocator's peak: LSE and D
+        "extra_bytes": int(peak_alloc - io_bytes),
+        "lse_and_D_bytes": int(4 * B * H * N * (2 if w.backward else 1)),
+        "inputs_outputs_bytes": int(io_bytes),
+        # free device memory before the first call minus after the timed steps: the
+        # library itself allocates nothing
+        "library_alloc_bytes": int(free_before - free_after),
+        # S and P of every head in 16-bit, as standard attention would hold them
+        "standard_S_P_bytes": int(B * H * metrics.score_and_prob_bytes_per_head(N)),
+    }
+    out = {
         "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
-                   "block_mask": w.mask, "backward": w.backward, "dropout": pdrop, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / peak, 2),
         "phases_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
         "phase_tflops": {"fwd": round(fwd_tf, 2), "bwd": round(bwd_tf, 2) if bwd_tf else None},
         "bytes_model": {"algorithmic_fwd": a_fwd, "algorithmic_bwd": a_bwd,
                         "standard_fwd": s_fwd, "standard_fwd_bwd": s_all},
+        "memory": memory,
         "roofline": roofline,
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "block_mask": w.mask, "backward": w.backward, "dropout": pdrop, "parallelism": "single GPU"},
     }
+    del q, k, v, o, lse, io
+    if w.backward:
+        del do, Dv, dq, dk, dv
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P for dense workloads (fa_fwd_dropout / fa_bwd_dropout); 0 = off")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other N >= 4096 workloads reported beside the default one")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import attn_inputs as ai
+
+    if args.workload in ai.PACKED_WORKLOADS:
+        return bench_packed(args, ai.PACKED_WORKLOADS[args.workload])
+    if args.workload not in ai.WORKLOADS:
+        log(f"unknown workload {args.workload}; choose from {list(ai.WORKLOADS) + list(ai.PACKED_WORKLOADS)}")
+        return 2
+    w = ai.WORKLOADS[args.workload]
+    pdrop = float(args.dropout)
+
+    log(f"[bench] drawing {w.name}")
+    dr = ai.draw_workload(w)
+    cpu = None
     if args.cpu_seconds > 0:
-        log(f"[bench] oracle CPU baseline ({args.cpu_seconds:.0f} s budget)")
-        result["cpu_baseline"] = cpu_baseline(w, dr, args.cpu_seconds, pdrop)
-    else:
-        result["cpu_baseline"] = None
+        # before any GPU use: the baseline's worker pool forks this process
+        log(f"[bench] oracle CPU baseline ({args.cpu_seconds:.0f} s budget, {cpu_pool_size()} workers)")
+        cpu = cpu_baseline(w, dr, args.cpu_seconds, pdrop)
+
+    head = run_dense(w, dr, args.steps, args.warmup, pdrop)
+    result = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": head["config"],
+    }
+    result.update({k: head[k] for k in ("pct_of_peak", "phases_ms", "phase_tflops", "bytes_model", "memory",
+                                        "roofline")})
+    result["cpu_baseline"] = cpu
+    if args.workload == DEFAULT_WORKLOAD and pdrop == 0 and not args.no_extra:
+        others = {}
+        for name in EXTRA_WORKLOADS:
+            wx = ai.WORKLOADS[name]
+            log(f"[bench] drawing {name}")
+            rx = run_dense(wx, ai.draw_workload(wx), args.steps, args.warmup)
+            others[name] = {k: rx[k] for k in ("value", "ms_per_step", "pct_of_peak", "phases_ms", "phase_tflops",
+                                               "roofline")}
+        result["other_workloads"] = others
     print(json.dumps(result), flush=True)
     return 0
 

@@ -19,8 +19,6 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # fp32 atomic add compiles to the hardware instruction
-    "-munsafe-fp-atomics",
     "-Wno-unused-command-line-argument",
 ]
 

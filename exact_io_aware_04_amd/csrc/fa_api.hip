@@ -24,10 +24,25 @@ fa_status check_shape(int B, int H, int N, int d) {
   // element count must fit comfortably in signed 64-bit
   const long double elems = (long double)B * H * (long double)N * d;
   if (elems > 9.0e18L) return FA_ERR_SHAPE;
-  // byte offsets inside one head (fp32 dQ accumulator included) are 32-bit
-  if ((long long)N * d * 4 >= (1LL << 31)) return FA_ERR_SHAPE;
+  // the kernels form byte offsets inside one head in 32-bit signed integers,
+  // also for the rows of a last tile that reach past N; N d < 2^29 keeps the
+  // head's 16-bit data below 1 GiB, with room for those rows (the largest
+  // accepted head is tested)
+  if ((long long)N * d >= (1LL << 29)) return FA_ERR_SHAPE;
   // the dispatch grid counts work-items in 32 bits: blocks * 256 threads < 2^32
   const long double blocks = (long double)B * H * ((N + 31) / 32 + 1);
+  if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// The D preprocess treats its input as rows x d with 64-bit row indices (dense
+// [B, H, N] rows, or the total_q x Hq rows of a packed batch): only the
+// dispatch grid (rows / (2048 / d) blocks of 256 work-items) limits it.
+fa_status check_preprocess_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const long double rows = (long double)B * H * (long double)N;
+  const long double blocks = ceill(rows / (2048.0L / d));
   if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;
   return FA_OK;
 }
@@ -154,12 +169,12 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_varlen");
 }
 
-fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
-                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
-                         int causal, int n_splits, float* o_partial, float* lse_partial, void* stream) {
-  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !o_partial || !lse_partial)
-    return FA_ERR_NULL;
+// Split-KV arguments other than the partial-result buffers.
+static fa_status splitkv_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                               int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d,
+                               fa_dtype dt, float scale, int n_splits) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
   FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
   if (n_splits < 1 || n_splits > FA_MAX_SPLITS) return FA_ERR_SHAPE;
   // group-packed rows (Hq / Hk heads x max_seqlen_q) index the grid in 32 bits
@@ -167,10 +182,15 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   if (blocks * 256.0L > 4.0e9L) return FA_ERR_SHAPE;
   FA_TRY(check_dtype(dt));
   FA_TRY(check_scale(scale));
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(o_partial) ||
-      !aligned16(lse_partial))
-    return FA_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
 
+static fa_status splitkv_launch(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                                int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt,
+                                float scale, int causal, int n_splits, float* o_partial, float* lse_partial,
+                                void* stream, const char* where) {
   fa::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.mask = nullptr;
@@ -188,13 +208,26 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   p.lse_part = lse_partial;
   p.n_splits = n_splits;
   p.part_rows = (long long)total_q * Hq;
-  return hip_status(fa::launch_fwd_splitkv(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_splitkv");
+  return hip_status(fa::launch_fwd_splitkv(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), where);
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                         int causal, int n_splits, float* o_partial, float* lse_partial, void* stream) {
+  FA_TRY(splitkv_check(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                       max_seqlen_k, Hq, Hk, d, dt, scale, n_splits));
+  if (!o_partial || !lse_partial) return FA_ERR_NULL;
+  if (!aligned16(o_partial) || !aligned16(lse_partial)) return FA_ERR_ALIGN;
+  return splitkv_launch(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                        max_seqlen_k, Hq, Hk, d, dt, scale, causal, n_splits, o_partial, lse_partial, stream,
+                        "fa_fwd_splitkv");
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N, int d, fa_dtype dt,
                             void* stream) {
   if (!o || !dO || !D) return FA_ERR_NULL;
-  FA_TRY(check_shape(B, H, N, d));
+  FA_TRY(check_preprocess_shape(B, H, N, d));
   FA_TRY(check_dtype(dt));
   if (!aligned16(o) || !aligned16(dO) || !aligned16(D)) return FA_ERR_ALIGN;
   const long long rows = (long long)B * H * N;

@@ -183,8 +183,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // ---------------------------------------------------------------------------
 // Buffer resources: 128-bit descriptors (base, byte range) held in SGPRs.
-// Loads past the range return zero and atomics past it are dropped, which
-// takes care of ragged tails without per-element branches.
+// Loads past the range return zero, which takes care of ragged tails without
+// per-element branches.
 // ---------------------------------------------------------------------------
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
@@ -196,9 +196,6 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_o
 }
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
-}
-__device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, int byte_off, float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

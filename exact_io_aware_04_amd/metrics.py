@@ -41,6 +41,21 @@ def kept_pairs_per_head(N: int, causal: bool, block_mask: Optional[np.ndarray], 
     return int(total)
 
 
+def kept_pairs_rows(rows, N: int, causal: bool, block_mask: Optional[np.ndarray], mask_block: int = 128) -> int:
+    """Kept (query, key) pairs of the given query rows of one head (N keys)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if block_mask is None:
+        per = np.minimum(rows + 1, N) if causal else np.full(rows.shape, N, dtype=np.int64)
+        return int(per.sum())
+    keep_tile = np.asarray(block_mask) != 0
+    total = 0
+    for i in rows:
+        for tj in np.nonzero(keep_tile[int(i) // mask_block])[0]:
+            c0, c1 = int(tj) * mask_block, min(N, (int(tj) + 1) * mask_block)
+            total += max(0, min(c1, int(i) + 1) - c0) if causal else c1 - c0
+    return int(total)
+
+
 def flops(B: int, H: int, pairs_per_head: int, d: int):
     """(forward, backward) algorithmic FLOPs for the whole batch."""
     pairs = B * H * pairs_per_head

@@ -53,7 +53,7 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,     /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,    /* B, H or N < 1, N*d >= 2^29 (per-head offsets are 32-bit), or the grid is too large */
+  FA_ERR_SHAPE = -2,    /* B, H or N < 1, N*d >= 2^29 (per-head byte offsets are 32-bit), or the grid is too large */
   FA_ERR_DTYPE = -3,    /* dt is not FA_F16 or FA_BF16 */
   FA_ERR_HEADDIM = -4,  /* d is not 64 or 128 */
   FA_ERR_MASK = -5,     /* block_mask given with mask_block != 128 */
@@ -73,7 +73,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  const uint8_t* block_mask, int mask_block, void* stream);
 
 /* Backward preprocess [P1 key design 3]: D[b,h,i] = sum_c dO[b,h,i,c] * o[b,h,i,c],
- * products and sum in float32, using the stored 16-bit o from fa_fwd. */
+ * products and sum in float32, using the stored 16-bit o from fa_fwd. The
+ * B*H*N rows are indexed in 64 bits (no per-head limit: a packed batch passes
+ * B = 1, H = Hq, N = total_q); FA_ERR_SHAPE only if the row count exceeds
+ * the dispatch grid (2^28 rows at d = 128, 2^29 at d = 64). */
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D,
                             int B, int H, int N, int d, fa_dtype dt, void* stream);
 

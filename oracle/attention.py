@@ -113,7 +113,8 @@ def forward_head(q, k, v, scale: float, causal: bool = False,
 
 def backward_head(q, k, v, do, scale: float, causal: bool = False,
                   block_mask: Optional[np.ndarray] = None, mask_block: int = 128,
-                  row_block: int = 1024, diag_offset: int = 0):
+                  row_block: int = 1024, diag_offset: int = 0,
+                  rows: Optional[Sequence[int]] = None):
     """Analytic gradients of O = softmax(scale q k^T) v for one head.
 
     With P the probabilities and dO the incoming gradient:
@@ -121,6 +122,9 @@ def backward_head(q, k, v, do, scale: float, causal: bool = False,
       dQ = scale dS K, dK = scale dS^T Q.
     Returns (dQ, dK, dV, D) in float64; D is computed from its definition as
     the row sum of P o dP (its equality with rowsum(dO o O) is a pin).
+    `rows` restricts the sums to those query rows: dQ and D are then filled
+    at those rows only (zero elsewhere) and dK, dV hold those rows'
+    contributions (every row's contribution is a separate term of the sums).
     """
     n = k.shape[0]
     cols = np.arange(n)
@@ -128,8 +132,9 @@ def backward_head(q, k, v, do, scale: float, causal: bool = False,
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dd = np.zeros(q.shape[0], dtype=np.float64)
-    for r0 in range(0, q.shape[0], row_block):
-        rr = np.arange(r0, min(r0 + row_block, q.shape[0]))
+    all_rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    for r0 in range(0, all_rows.size, row_block):
+        rr = all_rows[r0:r0 + row_block]
         keep = kept_pairs(rr, cols, causal, block_mask, mask_block, diag_offset)
         p, _ = _probabilities(_scores(q[rr], k, scale, keep))
         dv += p.T @ do[rr]

@@ -21,11 +21,17 @@ def test_more_than_one_gpu_exits_with_a_message():
 def test_cpu_baseline_object():
     w = ai.WORKLOADS["single_head_fwd_n256_d64_f16"]
     dr = ai.draw_workload(w)
-    cb = bench.cpu_baseline(w, dr, budget_s=0.01)
+    cb = bench.cpu_baseline(w, dr, budget_s=0.01, workers=2)
     assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s"
-    assert cb["value"] > 0 and cb["cores"] >= 1
-    assert "1 of 1 heads" in cb["sample"]
+    assert cb["value"] > 0 and cb["cores"] == 2
+    # two 128-row units, one per worker (each worker does at least one)
+    assert "2 of 2 (head, 128-query-row block) units" in cb["sample"]
+
+
+def test_cpu_pool_size_follows_the_affinity_mask():
+    n = bench.cpu_pool_size()
+    assert 1 <= n <= 16 and n <= len(os.sched_getaffinity(0))
 
 
 def test_traffic_is_null_unless_taken_on_these_sources(tmp_path, monkeypatch):

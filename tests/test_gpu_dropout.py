@@ -10,7 +10,8 @@ import pytest
 
 import attn_inputs as ai
 import oracle.dropout as od
-from harness import GRAD_REL_TOL, LSE_TOL, O_TOL, from_dev, rel_fro, say, to_dev
+from error_model import gradient_scales_head
+from harness import LSE_TOL, O_TOL, check_grads, from_dev, report, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +54,10 @@ def test_dropout_parity(n, d, dtype, mode, p):
         assert (np.isneginf(res["lse"][0, h]) == ~live).all(), what
         if live.any():
             assert float(np.abs(res["lse"][0, h][live] - lse_ref[live]).max()) <= LSE_TOL[dtype], what
-        for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
-            e = rel_fro(res[name][0, h], ref)
-            assert e <= GRAD_REL_TOL, f"{what}: {name} relative error {e:.3e}"
+        z = lambda rows, cols, h=h: od.keep_mask(h, rows, cols, p, SEED + seed, 3) / (1.0 - p)
+        scales = gradient_scales_head(q, k, v, do, scale, causal, mask, 128, z=z)
+        report(what, check_grads({n_: res[n_][0, h] for n_ in ("dq", "dk", "dv")}, {"dq": dq, "dk": dk, "dv": dv},
+                                 what, scales, dtype))
 
 
 @pytest.mark.parametrize("d", [64, 128])

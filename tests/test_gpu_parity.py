@@ -11,8 +11,9 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from harness import (GRAD_REL_TOL, LSE_TOL, check_D, check_forward, check_grads, from_dev, rel_fro,
-                     run_gpu, say, to_dev)
+from harness import (GRAD_REL_TOL, LSE_TOL, O_TOL, check_D, check_forward, check_grads, from_dev, rel_fro,
+                     report, run_gpu, say, to_dev)
+from error_model import UNIT_ROUNDOFF, gradient_scales_head
 
 pytestmark = pytest.mark.gpu
 
@@ -27,13 +28,20 @@ def _mask_for(mode, n, seed):
 
 
 def _oracle_head(dr, b, h, scale, causal, mask, backward=True):
+    """Oracle O, LSE (and dQ, dK, dV, D) of head (b, h), plus the gradients'
+    element-wise error scales under "scales"."""
     q, k, v = (dr.f64(n, b, h) for n in "qkv")
     o, lse = oracle.forward_head(q, k, v, scale, causal, mask, 128)
     out = {"o": o, "lse": lse}
     if backward:
         do = dr.f64("do", b, h)
         out["dq"], out["dk"], out["dv"], out["D"] = oracle.backward_head(q, k, v, do, scale, causal, mask, 128)
+        out["scales"] = gradient_scales_head(q, k, v, do, scale, causal, mask, 128)
     return out
+
+
+def _grads(res, b, h):
+    return {k: res[k][b, h] for k in ("dq", "dk", "dv")}
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -53,7 +61,7 @@ def test_small_shapes(n, d, dtype, mode):
         ref = _oracle_head(dr, 0, h, scale, causal, mask)
         what = f"N={n} d={d} {dtype} {mode} h={h}"
         check_forward(res["o"][0, h], res["lse"][0, h], ref["o"], ref["lse"], dtype, what)
-        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, 0, h), ref, what, ref["scales"], dtype))
         check_D(res["D"][0, h], dr.f64("do", 0, h), o_dev[0, h], what)
 
 
@@ -94,8 +102,10 @@ def test_running_max_keeps_rising(d, dtype, causal):
     # O bound for a softmax this peaked: the PV product consumes the probabilities
     # rounded to the operand type (RNE, unit roundoff u), which moves O_ic by at most
     # u sum_j P_ij |V_jc - O_ic| <= u ((P |V|)_ic + |O_ic|) (the weights stay
-    # normalised), and O itself is rounded (u |O_ic|). A wrong rescale factor errs by O(1).
-    u = 2.0 ** -11 if dtype == ai.F16 else 2.0 ** -8
+    # normalised), and O itself is rounded (u |O_ic|). A wrong rescale factor errs by
+    # O(1). Where that rounding bound is within the stated O tolerance (2e-3 fp16,
+    # 1e-2 bf16), the stated tolerance itself is asserted.
+    u = UNIT_ROUNDOFF[dtype]
     for h in range(2):
         ref = _oracle_head(dr, 0, h, scale, causal, None)
         what = f"rescale N={n} d={d} {dtype} causal={causal} h={h}"
@@ -107,10 +117,15 @@ def test_running_max_keeps_rising(d, dtype, causal):
         bound = u * (p @ np.abs(v) + 2.0 * np.abs(ref["o"])) + 1e-4
         o = res["o"][0, h]
         assert np.isfinite(o).all(), what
-        assert (np.abs(o - ref["o"]) <= bound).all(), \
-            f"{what}: O error {np.abs(o - ref['o']).max():.3e} beyond the rounding bound"
+        err = np.abs(o - ref["o"])
+        inside = bound <= O_TOL[dtype]
+        say(f"    {what}: O max-abs error {err.max():.3e} (rounding bound up to {bound.max():.3e}); "
+            f"{inside.mean() * 100:.1f}% of elements have a bound within {O_TOL[dtype]:g}, "
+            f"max error there {err[inside].max() if inside.any() else 0.0:.3e}")
+        assert (err <= bound).all(), f"{what}: O error {err.max():.3e} beyond the rounding bound"
+        assert (err[inside] <= O_TOL[dtype]).all(), f"{what}: O error beyond the stated tolerance"
         assert np.abs(res["lse"][0, h] - ref["lse"]).max() <= LSE_TOL[dtype], f"{what}: LSE"
-        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, 0, h), ref, what, ref["scales"], dtype))
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -126,7 +141,7 @@ def test_fully_masked_rows(causal, dtype):
     ref = _oracle_head(dr, 0, 0, scale, causal, mask)
     check_forward(res["o"][0, 0], res["lse"][0, 0], ref["o"], ref["lse"], dtype, "masked rows")
     assert (res["o"][0, 0, 128:256] == 0).all()
-    check_grads({k: res[k][0, 0] for k in ("dq", "dk", "dv")}, ref, "masked rows")
+    report("masked rows", check_grads(_grads(res, 0, 0), ref, "masked rows", ref["scales"], dtype))
     assert (res["dq"][0, 0, 128:256] == 0).all()
 
 
@@ -150,10 +165,11 @@ def test_mask_rows_longer_than_2048_tiles(d):
         a, b = 256 * grp, min(256 * grp + 256, n)
         o, lse = oracle.forward_head(q[a:b], k[a:b], v[a:b], scale, False)
         dq, dk, dv, _ = oracle.backward_head(q[a:b], k[a:b], v[a:b], do[a:b], scale, False)
+        scales = gradient_scales_head(q[a:b], k[a:b], v[a:b], do[a:b], scale, False)
         what = f"group {grp} (rows {a}..{b - 1})"
         check_forward(res["o"][0, 0, a:b], res["lse"][0, 0, a:b], o, lse, ai.F16, what)
-        check_grads({"dq": res["dq"][0, 0, a:b], "dk": res["dk"][0, 0, a:b], "dv": res["dv"][0, 0, a:b]},
-                    {"dq": dq, "dk": dk, "dv": dv}, what)
+        report(what, check_grads({"dq": res["dq"][0, 0, a:b], "dk": res["dk"][0, 0, a:b], "dv": res["dv"][0, 0, a:b]},
+                                 {"dq": dq, "dk": dk, "dv": dv}, what, scales, ai.F16))
 
 
 @pytest.mark.parametrize("d,dtype,causal", [(64, ai.F16, False), (128, ai.BF16, True)])
@@ -175,8 +191,10 @@ def test_random_mask_across_mask_words(d, dtype, causal):
     check_forward(res["o"][0, 0, rows], res["lse"][0, 0, rows], o_ref, lse_ref, dtype, "sampled rows")
     say(f"[mask 130 tiles] oracle gradients at {rows.size} rows / columns")
     dq, dk, dv, _ = oracle.backward_head_sampled(q, k, v, do, scale, causal, mask, 128, rows, rows)
-    check_grads({"dq": res["dq"][0, 0, rows], "dk": res["dk"][0, 0, rows], "dv": res["dv"][0, 0, rows]},
-                {"dq": dq, "dk": dk, "dv": dv}, "sampled rows / columns")
+    scales = gradient_scales_head(q, k, v, do, scale, causal, mask, 128, q_rows=rows, k_cols=rows)
+    report("sampled rows / columns",
+           check_grads({"dq": res["dq"][0, 0, rows], "dk": res["dk"][0, 0, rows], "dv": res["dv"][0, 0, rows]},
+                       {"dq": dq, "dk": dk, "dv": dv}, "sampled rows / columns", scales, dtype))
     for name in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[name]).all(), f"non-finite {name}"
 
@@ -195,7 +213,7 @@ def test_grid_with_partial_round_of_heads(causal):
         ref = _oracle_head(dr, 0, h, scale, causal, None)
         what = f"head {h}"
         check_forward(res["o"][0, h], res["lse"][0, h], ref["o"], ref["lse"], ai.F16, what)
-        check_grads({k: res[k][0, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, 0, h), ref, what, ref["scales"], ai.F16))
 
 
 def test_forward_is_bitwise_deterministic():
@@ -293,7 +311,7 @@ def test_full_gpt2_medium_shape():
         ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
         what = f"{w.name} head ({b},{h})"
         check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
-        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, b, h), ref, what, ref["scales"], w.dtype))
     assert np.isfinite(res["o"]).all() and np.isfinite(res["dq"]).all()
 
 
@@ -304,19 +322,19 @@ def test_full_causal_8k():
         ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
         what = f"{w.name} head ({b},{h})"
         check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
-        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, b, h), ref, what, ref["scales"], w.dtype))
     for n in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[n]).all()
 
 
 def test_full_butterfly_16k():
     w, dr, mask, res = _full_run("butterfly_b4_h16_n16384_d64_f16")
-    for b, h in [(3, 5)]:
+    for b, h in [(3, 5), (0, 11)]:
         say(f"[full] {w.name}: oracle head ({b},{h})")
         ref = _oracle_head(dr, b, h, w.scale, w.causal, mask)
         what = f"{w.name} head ({b},{h})"
         check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], w.dtype, what)
-        check_grads({k: res[k][b, h] for k in ("dq", "dk", "dv")}, ref, what)
+        report(what, check_grads(_grads(res, b, h), ref, what, ref["scales"], w.dtype))
     for n in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[n]).all()
 
@@ -339,8 +357,10 @@ def test_full_causal_64k_sampled():
         check_forward(res["o"][0, h, rows], res["lse"][0, h, rows], o_ref, lse_ref, w.dtype, f"{w.name} h{h}")
         dq, dk, dv, _ = oracle.backward_head_sampled(q, k, v, do, w.scale, True, None, 128, rows, cols,
                                                      first_row=N - 2048)
-        check_grads({"dq": res["dq"][0, h, rows], "dk": res["dk"][0, h, cols], "dv": res["dv"][0, h, cols]},
-                    {"dq": dq, "dk": dk, "dv": dv}, f"{w.name} h{h} sampled")
+        scales = gradient_scales_head(q, k, v, do, w.scale, True, q_rows=rows, k_cols=cols, first_row=N - 2048)
+        report(f"{w.name} h{h} sampled",
+               check_grads({"dq": res["dq"][0, h, rows], "dk": res["dk"][0, h, cols], "dv": res["dv"][0, h, cols]},
+                           {"dq": dq, "dk": dk, "dv": dv}, f"{w.name} h{h} sampled", scales, w.dtype))
         # invariants over the whole head (hold for any N)
         sum_dv, sum_do = res["dv"][0, h].sum(axis=0), do.sum(axis=0)
         assert rel_fro(sum_dv, sum_do) <= GRAD_REL_TOL
@@ -348,6 +368,27 @@ def test_full_causal_64k_sampled():
         assert np.linalg.norm(sum_dk) <= 1e-2 * np.abs(res["dk"][0, h]).sum(axis=0).max()
     for n in ("o", "dq", "dk", "dv"):
         assert np.isfinite(res[n]).all()
+
+
+@pytest.mark.timeout(900)
+def test_full_causal_64k_early_key_columns():
+    """N = 65536, early key columns: key j is seen by every query i >= j, so
+    dK_j and dV_j of j near 0 sum over up to 65536 rows, the longest loops of
+    the dK/dV kernel (up to 1024 query tiles per key block). The oracle needs
+    LSE_i and D_i of every row for them (a full forward of one head in
+    float64), so this runs on one head."""
+    w, dr, mask, res = _full_run("causal_b1_h8_n65536_d128_bf16")
+    N, h = w.N, 3
+    cols = np.array([0, 1, 63, 64, 127, 128, 4095, 32767])
+    rows = np.array([0, 1, 64, 4095])
+    say(f"[full] {w.name}: oracle (all {N} rows) for key columns {cols.tolist()} of head {h}")
+    q, k, v, do = (dr.f64(n, 0, h) for n in ("q", "k", "v", "do"))
+    dq, dk, dv, _ = oracle.backward_head_sampled(q, k, v, do, w.scale, True, None, 128, rows, cols, first_row=0)
+    say(f"[full] {w.name}: error scales for head {h}")
+    scales = gradient_scales_head(q, k, v, do, w.scale, True, q_rows=rows, k_cols=cols, first_row=0)
+    report(f"{w.name} h{h} early columns",
+           check_grads({"dq": res["dq"][0, h, rows], "dk": res["dk"][0, h, cols], "dv": res["dv"][0, h, cols]},
+                       {"dq": dq, "dk": dk, "dv": dv}, f"{w.name} h{h} early columns", scales, w.dtype))
 
 
 def test_largest_head_d128_causal():
@@ -391,6 +432,9 @@ def test_largest_head_d128_causal():
     check_forward(got["o"], got["lse"], o_ref, lse_ref, ai.BF16, "largest head")
     gq, gk, gv, _ = oracle.backward_head_sampled(q64, k64, v64, do64, scale, True, None, 128, rows, cols,
                                                  first_row=first, row_block=16)
-    check_grads({"dq": got["dq"], "dk": got["dk"], "dv": got["dv"]}, {"dq": gq, "dk": gk, "dv": gv},
-                "largest head sampled")
+    scales = gradient_scales_head(q64, k64, v64, do64, scale, True, q_rows=rows, k_cols=cols, first_row=first,
+                                  row_block=16)
+    report("largest head sampled",
+           check_grads({"dq": got["dq"], "dk": got["dk"], "dv": got["dv"]}, {"dq": gq, "dk": gk, "dv": gv},
+                       "largest head sampled", scales, ai.BF16))
 

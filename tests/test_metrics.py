@@ -64,3 +64,20 @@ def test_varlen_pair_count_matches_oracle_visibility():
                     for a, b in zip(lq, lk))
         assert metrics.kept_pairs_varlen(lq, lk, causal) == brute
     assert metrics.kept_pairs_varlen([1], [4096], True) == 4096      # decode: one query sees every key
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("masked", [False, True])
+def test_pairs_of_selected_rows_match_brute_force(causal, masked):
+    n, bs = 300, 128
+    mask = ai.random_block_mask(3, 0.5, 9) if masked else None
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    keep = np.ones((n, n), dtype=bool)
+    if causal:
+        keep &= j <= i
+    if mask is not None:
+        keep &= (np.asarray(mask) != 0)[i // bs, j // bs]
+    rows = np.array([0, 1, 127, 128, 200, 299])
+    assert metrics.kept_pairs_rows(rows, n, causal, mask, bs) == int(keep[rows].sum())
+    assert metrics.kept_pairs_rows(np.arange(n), n, causal, mask, bs) == metrics.kept_pairs_per_head(n, causal, mask, bs)

@@ -382,6 +382,30 @@ def test_sampled_backward_matches_whole_head(causal, masked):
             oracle.backward_head_sampled(q, k, v, g, 0.35, causal, bm, bs, rows, cols, first_row=40)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_subsets_partition_the_backward(causal):
+    """Each query row adds its own terms to dK and dV: the backward restricted
+    to disjoint row subsets sums to the whole-head backward, and dQ / D of a
+    subset's rows are the whole head's."""
+    n, d = 50, 6
+    q, k, v, g = (rand((n, d), 160 + i) for i in range(4))
+    whole = oracle.backward_head(q, k, v, g, 0.45, causal)
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(n)
+    parts = [np.sort(perm[:17]), np.sort(perm[17:30]), np.sort(perm[30:])]
+    acc_k, acc_v = np.zeros_like(k), np.zeros_like(v)
+    for rows in parts:
+        dq, dk, dv, D = oracle.backward_head(q, k, v, g, 0.45, causal, row_block=4, rows=rows)
+        np.testing.assert_allclose(dq[rows], whole[0][rows], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(D[rows], whole[3][rows], rtol=1e-12, atol=1e-14)
+        others = np.setdiff1d(np.arange(n), rows)
+        assert (dq[others] == 0).all() and (D[others] == 0).all()
+        acc_k += dk
+        acc_v += dv
+    np.testing.assert_allclose(acc_k, whole[1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(acc_v, whole[2], rtol=1e-11, atol=1e-12)
+
+
 def test_batched_helpers_loop_over_heads():
     B, H, n, d = 2, 3, 10, 4
     q, k, v, g = (rand((B, H, n, d), 150 + i) for i in range(4))
