@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
@@ -224,6 +226,61 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                         "fa_fwd_splitkv");
 }
 
+// ---------------------------------------------------------------------------
+// Split-KV without allocation: the partial results live in this file-scope
+// device array instead of caller-provided workspace. Each GPU the library runs
+// on holds its own copy (FA_NOALLOC_SCRATCH_BYTES) until the process ends. In
+// host code `scratch` only names the symbol; its device address is looked up
+// with hipGetSymbolAddress once per device (that device current) and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch` (looked up on the first call per device).
+fa_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "fa_fwd_splitkv_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    fprintf(stderr, "libfa: fa_fwd_splitkv_noalloc: device %d beyond the %d the library tracks\n", dev, kMaxDevices);
+    return FA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "fa_fwd_splitkv_noalloc: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+}  // namespace
+
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                                 int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt,
+                                 float scale, int causal, int n_splits, void* stream) {
+  FA_TRY(splitkv_check(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                       max_seqlen_k, Hq, Hk, d, dt, scale, n_splits));
+  // partials: o [n_splits, total_q, Hq, d] at offset 0, lse [n_splits, total_q, Hq] after it (256-byte aligned)
+  const size_t rows = (size_t)n_splits * (size_t)total_q * (size_t)Hq;
+  const size_t o_bytes = (rows * (size_t)d * 4 + 255) & ~(size_t)255;
+  if (o_bytes + rows * 4 > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* base = nullptr;
+  FA_TRY(scratch_address(&base));
+  // every partial the merge reads is written by its split first: nothing to clear
+  float* o_part = reinterpret_cast<float*>(base);
+  float* lse_part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(base) + o_bytes);
+  return splitkv_launch(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                        max_seqlen_k, Hq, Hk, d, dt, scale, causal, n_splits, o_part, lse_part, stream,
+                        "fa_fwd_splitkv_noalloc");
+}
+
 fa_status fa_bwd_preprocess(const void* o, const void* dO, float* D, int B, int H, int N, int d, fa_dtype dt,
                             void* stream) {
   if (!o || !dO || !D) return FA_ERR_NULL;
@@ -324,6 +381,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP kernel launch failed";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_DROPOUT: return "FA_ERR_DROPOUT: dropout probability must satisfy 0 <= p < 1";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: split-KV partial results exceed the library's static scratch (FA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown fa_status";
 }

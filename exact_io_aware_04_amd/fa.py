@@ -28,10 +28,12 @@ FA_OK = 0
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE", -4: "FA_ERR_HEADDIM",
     -5: "FA_ERR_MASK", -6: "FA_ERR_ALIGN", -7: "FA_ERR_HIP", -8: "FA_ERR_SCALE", -9: "FA_ERR_DROPOUT",
+    -10: "FA_ERR_SCRATCH",
 }
 EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
-            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_status_string")
+            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_status_string")
 FA_MAX_SPLITS = 256
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def _load() -> ctypes.CDLL:
@@ -63,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, vp, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i]
     return lib
@@ -122,6 +126,18 @@ def fa_fwd_splitkv(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, 
                    causal, n_splits, o_partial, lse_partial, stream) -> int:
     return _lib.fa_fwd_splitkv(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
                                scale, causal, n_splits, o_partial, lse_partial, stream)
+
+
+def splitkv_noalloc_bytes(total_q: int, hq: int, d: int, n_splits: int) -> int:
+    """Scratch bytes fa_fwd_splitkv_noalloc needs (it refuses more than FA_NOALLOC_SCRATCH_BYTES)."""
+    rows = n_splits * total_q * hq
+    return ((rows * d * 4 + 255) & ~255) + rows * 4
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
+                           scale, causal, n_splits, stream) -> int:
+    return _lib.fa_fwd_splitkv_noalloc(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk,
+                                       d, dt, scale, causal, n_splits, stream)
 
 
 def fa_status_string(status: int) -> str:

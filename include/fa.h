@@ -60,7 +60,8 @@ typedef enum {
   FA_ERR_ALIGN = -6,    /* a tensor pointer is not 16-byte aligned */
   FA_ERR_HIP = -7,      /* a HIP launch reported an error */
   FA_ERR_SCALE = -8,    /* scale is not finite and > 0 */
-  FA_ERR_DROPOUT = -9   /* dropout probability outside [0, 1) */
+  FA_ERR_DROPOUT = -9,  /* dropout probability outside [0, 1) */
+  FA_ERR_SCRATCH = -10  /* fa_fwd_splitkv_noalloc: partial results beyond FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Forward [P1 key designs 1-2; P3 forward process].
@@ -176,6 +177,29 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
                          int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
                          int causal, int n_splits, float* o_partial, float* lse_partial, void* stream);
+
+/* Split-KV forward that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Same arguments, result and
+ * conventions as fa_fwd_splitkv, without o_partial / lse_partial: the partial
+ * results live in a static device array of FA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends. The call makes no
+ * allocation of any kind (its first call on a device looks the array's
+ * address up once).
+ *   Limit: the partial results, R * d * 4 bytes rounded up to a multiple of
+ *   256 plus R * 4 bytes with R = n_splits * total_q * Hq, must fit in
+ *   FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_SCRATCH (checked before any HIP
+ *   call; nothing enqueued). E.g. 8 splits of 32 decode rows x 32 query heads
+ *   at d = 128 use 4.2 MB of the 32 MiB.
+ *   Every call on a GPU shares that GPU's array: calls that may overlap on one
+ *   GPU (other streams, other host threads) race and must be serialised by the
+ *   caller. The array keeps the last call's contents; no part of it needs to
+ *   start at any particular value. */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                                 int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt,
+                                 float scale, int causal, int n_splits, void* stream);
 
 /* Gradients for fa_fwd_varlen. dk, dv of a key/value head sum the
  * contributions of every query head that reads it (computed inside one
