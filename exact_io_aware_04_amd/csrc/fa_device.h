@@ -292,6 +292,13 @@ __device__ __forceinline__ uint32_t span_bytes(int rows, int stride, int width, 
 // between rounds. Counter-based: the dropout mask is a pure function of
 // (counter, key), so the backward regenerates the forward's mask.
 // ---------------------------------------------------------------------------
+// a ^ b ^ k in one instruction (gfx950 three-input bitwise op, truth table 0x96);
+// k is uniform (a key word)
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                               uint32_t k1) {
 #pragma unroll
@@ -300,10 +307,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
+    // the key schedule is uniform: advance it in scalar registers each round
+    // (hoisted out of the tile loop, its 20 words were kept in vector lanes)
+    asm volatile("" : "+s"(k0), "+s"(k1));
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3_key((uint32_t)(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3_key((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;

@@ -29,6 +29,10 @@ namespace fa {
 // Rescale the running state only when the running maximum grows by more than
 // this (log2 units); between rescales probabilities stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+// Probabilities below 2^kRescaleThreshold: a lane's share of a tile's row sum at
+// or below this bounds every one of its probabilities by the same amount.
+constexpr float kPartialSumLimit = 256.0f;
+static_assert(kPartialSumLimit == (float)(1 << (int)kRescaleThreshold), "bound of the rescale rule");
 
 // SPLIT = false: one workgroup = NW*32 query rows of one (sequence, head), all
 // kept key tiles; writes O and LSE.
@@ -41,11 +45,11 @@ constexpr float kRescaleThreshold = 8.0f;
 // DROP: dropout on P after the softmax (dense layout, not with SPLIT): the row
 // sum uses the undropped probabilities, the product P V the dropped ones, and
 // the epilogue applies 1 / (1 - p) with the normalisation.
-// Register target (minimum waves per SIMD): three at d = 64 without dropout
-// (<= 168 VGPRs; the kernel fits in 128, so four run), two at d = 64 with the
-// dropout generator inlined (165 VGPRs, so three run) and at d = 128.
+// Register target (minimum waves per SIMD): four at d = 64 without dropout
+// (<= 128 VGPRs), two at d = 64 with the dropout generator inlined (170 VGPRs,
+// so three run) and at d = 128.
 template <int D, bool DROP>
-struct FwdOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 3 : 2; };
+struct FwdOccupancy { static constexpr int value = (D <= 64 && !DROP) ? 4 : 2; };
 
 template <class DT, int D, int BN, int NW, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_kernel(FwdParams p) {
@@ -164,24 +168,25 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
   if (j < j_end) gload(j, 0);
   wait_tile_copies();
   __syncthreads();
-  int buf = 0;
 
   // a wave with no row of its sequence (split-KV decode: G * n_q rows of 128) only
   // takes its part in the copies and barriers
   const bool wave_live = q0 + __builtin_amdgcn_readfirstlane(wave) * 32 < nrows;
 
-  while (j < j_end) {
+  // One key tile. The loop runs two of these per turn, one per LDS buffer, so
+  // that every operand address is a per-lane offset plus an immediate.
+  auto step = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int jn = next_kept(j + 1);
-    if (jn < j_end) gload(jn, buf ^ 1);     // that buffer was last read before the previous barrier
+    if (jn < j_end) gload(jn, BUF ^ 1);       // that buffer was last read before the previous barrier
     if (!wave_live) {
       wait_tile_copies();
       __syncthreads();
-      buf ^= 1;
       j = jn;
-      continue;
+      return;
     }
 
-    const char* kt = smem + buf * 2 * TILE;
+    const char* kt = smem + BUF * 2 * TILE;
     const char* vt = kt + TILE;
     const int k0 = j * BN;
 
@@ -204,39 +209,58 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
         }
     }
 
-    // row maximum of this tile (raw scores; the scale is positive)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NS; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    const float m_tile = pair_max(mx) * c2;
-    const bool need = m_tile > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
-      if (need) m_run = m_tile;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT32; ++t) acc[t] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // probabilities relative to m_use, packed as B operands of O^T += V^T P^T;
-    // the row-sum share adds exactly the rounded values the product uses
+    // probabilities relative to the reference m_use, packed as B operands of
+    // O^T += V^T P^T; returns this lane's share of their sum, which adds
+    // exactly the rounded values the product uses
     V8 pb[NS][2];
+    auto probs = [&](float m_use) {
+      float lt = 0.f;
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      float e[16];
+      for (int t = 0; t < NS; ++t) {
+        float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c2, -m_use));
-      pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-      l_run = sum8<DT>(pb[t][0], l_run);
-      l_run = sum8<DT>(pb[t][1], l_run);
-      if constexpr (DROP) {
+        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[t][r], c2, -m_use));
+        pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        pb[t][1] = pack8<DT>(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+        lt = sum8<DT>(pb[t][0], lt);
+        lt = sum8<DT>(pb[t][1], lt);
+      }
+      return lt;
+    };
+    // Common case: the probabilities against the current reference stay at or
+    // below 2^threshold, which this lane's share of their sum bounds; the tile
+    // maximum is then not needed. Otherwise (first tile of the row, or a share
+    // above the bound): the tile maximum, a rescale if it grew by more than
+    // the threshold (the reference point is arbitrary: exact), and the
+    // probabilities again.
+    float lt = m_run == -INFINITY ? INFINITY : probs(m_run);
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kPartialSumLimit))) {
+      float mx = -INFINITY;               // row maximum of this tile (raw scores; the scale is positive)
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      const float m_tile = pair_max(mx) * c2;
+      const bool need = m_tile > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+        if (need) m_run = m_tile;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT32; ++t) acc[t] *= alpha;
+      }
+      lt = probs((m_run == -INFINITY) ? 0.f : m_run);
+    }
+    l_run += lt;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
         // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u: two generator calls
         // per lane, shared with the lane that holds the other query of the row pair
         const uint32_t kb16 = keep16_pair(p.drop, (uint32_t)((k0 + 32 * t) >> 2), (uint32_t)qw, (uint32_t)bh, lane);
+        float e[16];
+        unpack8<DT>(pb[t][0], e);
+        unpack8<DT>(pb[t][1], e + 8);
 #pragma unroll
         for (int r = 0; r < 16; ++r) e[r] = ((kb16 >> r) & 1) ? e[r] : 0.f;
         pb[t][0] = pack8<DT>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
@@ -257,8 +281,12 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
 
     wait_tile_copies();
     __syncthreads();
-    buf ^= 1;
     j = jn;
+  };
+  while (j < j_end) {
+    step(std::integral_constant<int, 0>{});
+    if (j >= j_end) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O = O~ / l, LSE = m ln2 + ln l
