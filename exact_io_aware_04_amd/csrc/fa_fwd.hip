@@ -408,6 +408,10 @@ hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {
       return is_bf16 ? launch_fwd_t<BF16, 64, 64, 8>(p, st) : launch_fwd_t<F16, 64, 64, 8>(p, st);
     return is_bf16 ? launch_fwd_t<BF16, 64, 64, 4>(p, st) : launch_fwd_t<F16, 64, 64, 4>(p, st);
   }
+  // d = 128 without block mask or dropout: 8-wave workgroups (256 query rows) share
+  // each K/V tile (causal N=65536: 7.75 -> 7.50 ms, N=8192: 1.10 -> 1.08 ms)
+  if (p.mask == nullptr && !p.drop.on)
+    return is_bf16 ? launch_fwd_t<BF16, 128, 64, 8>(p, st) : launch_fwd_t<F16, 128, 64, 8>(p, st);
   return is_bf16 ? launch_fwd_t<BF16, 128, 64, 4>(p, st) : launch_fwd_t<F16, 128, 64, 4>(p, st);
 }
 
