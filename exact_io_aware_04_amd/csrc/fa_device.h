@@ -391,6 +391,21 @@ __device__ __forceinline__ void unpack8(typename DT::V8 v, float* f) {
   for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
 }
 
+// Zero the 16-bit values of an operand register set whose bit in `bits` (bit i
+// for value i) is clear, on the packed words: a kept value keeps its bits, a
+// dropped one becomes +0, as if it were zeroed before rounding.
+template <class DT>
+__device__ __forceinline__ typename DT::V8 keep_mask8(typename DT::V8 v, uint32_t bits) {
+  u32x4 w = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (uint32_t)((int32_t)(bits << (31 - 2 * i)) >> 31);   // all ones iff bit 2i
+    const uint32_t hi = (uint32_t)((int32_t)(bits << (30 - 2 * i)) >> 31);   // all ones iff bit 2i + 1
+    w[i] &= (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(typename DT::V8, w);
+}
+
 // Sum of the 8 16-bit values of an operand register set, accumulated in fp32.
 template <class DT>
 __device__ __forceinline__ float sum8(typename DT::V8 v, float acc);
