@@ -19,9 +19,9 @@ identical keys, the causal first row, finite differences, the D identity,
 special cases, gradient invariants, mask reductions and permutation
 equivariance. Packed variable-length batches are in oracle/varlen.py and
 dropout in oracle/dropout.py (tests/test_oracle_varlen.py,
-tests/test_oracle_dropout.py). The one "parity unpinned" item is the bit
-pattern of the dropout generator (Philox4x32-10): only its statistical
-properties are pinned, and the GPU must reproduce it bit for bit.
+tests/test_oracle_dropout.py). The dropout generator (Philox4x32-10) is
+pinned to rocRAND's implementation of the same function, run on the host, and
+the GPU must reproduce it bit for bit. No function is left unpinned.
 """
 from .attention import (  # noqa: F401
     kept_pairs,

@@ -27,9 +27,10 @@ offset), key = (seed mod 2^32, seed div 2^32)); it is dropped iff that half
 The kept fraction is 1 - floor(p 2^16) / 2^16, within 2^-16 of 1 - p; the
 rescale stays 1 / (1 - p) as the method states. For a packed batch,
 bh = b H + h and i, j are positions inside sequence b.
-The generator's bit pattern is "parity unpinned": no published output is
-reproduced here; its pins are statistical (keep rate, uniformity, counter
-and key sensitivity) and the GPU must match this implementation bit for bit.
+The generator is pinned to rocRAND's own Philox4x32-10 (its header
+implementation, run on the host) at random counters and keys, and
+statistically (keep rate, uniformity, counter and key sensitivity); the GPU
+must match this implementation bit for bit.
 """
 from __future__ import annotations
 

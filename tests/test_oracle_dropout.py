@@ -3,10 +3,16 @@
 The attention math with a given mask is pinned by p = 0 reducing to the plain
 oracle, finite differences with the mask held fixed, the D identity, the
 unchanged LSE and unbiasedness (the mean output over many seeds approaches
-the output without dropout). The generator's bit pattern is parity unpinned;
-its statistical properties are pinned: keep rate, byte uniformity,
+the output without dropout). The generator's bit pattern is pinned to a
+library routine: rocRAND's header implementation of Philox4x32-10, compiled
+here for the host (tests/philox_rocrand_ref.cpp), at random counters and keys.
+Its statistical properties are pinned too: keep rate, byte uniformity,
 determinism and sensitivity to every counter and key field.
 """
+import os
+import shutil
+import subprocess
+
 import numpy as np
 import pytest
 
@@ -39,6 +45,37 @@ def test_keep_rate(p):
     n = m.size
     sigma = np.sqrt(n * p * (1 - p))
     assert abs(m.sum() - n * (1 - p)) <= 5 * sigma
+
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None, reason="hipcc is needed to build the rocRAND host reference")
+def test_philox_matches_rocrand(tmp_path):
+    """The oracle's generator equals rocRAND's Philox4x32-10 (a separate
+    implementation of the same published function) on 400 random counters and
+    keys, including counters with all four words nonzero and keys above 2^32."""
+    src = os.path.join(os.path.dirname(__file__), "philox_rocrand_ref.cpp")
+    exe = str(tmp_path / "philox_ref")
+    r = subprocess.run([HIPCC, "-O1", "-x", "hip", "--offload-arch=gfx950", src, "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    rng = np.random.default_rng(5)
+    n = 400
+    seeds = rng.integers(0, 2 ** 64, n, dtype=np.uint64)
+    ctr = rng.integers(0, 2 ** 32, (n, 4), dtype=np.uint64)
+    ctr[:, 1] &= np.uint64(2 ** 30 - 1)             # the reference takes (c0, c1) as 4 (c0 + 2^32 c1) in 64 bits
+    ctr[:50] = 0                                   # small counters (the kernels' row / column blocks)
+    ctr[:50, 0] = np.arange(50)
+    seeds[:5] = [0, 1, 1234, 2 ** 32, 2 ** 64 - 1]
+    lines = "".join(f"{int(s)} {int(a)} {int(b)} {int(c)} {int(d)}\n" for s, (a, b, c, d) in zip(seeds, ctr))
+    out = subprocess.run([exe], input=lines, capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0
+    ref = np.array([[int(x) for x in l.split()] for l in out.stdout.splitlines()], dtype=np.uint64)
+    assert ref.shape == (n, 4)
+    got = od.philox4x32_10(ctr[:, 0], ctr[:, 1], ctr[:, 2], ctr[:, 3], seeds & np.uint64(0xFFFFFFFF),
+                           seeds >> np.uint64(32))
+    np.testing.assert_array_equal(np.stack(got, axis=1).astype(np.uint64), ref)
 
 
 def test_word_bytes_uniform():
