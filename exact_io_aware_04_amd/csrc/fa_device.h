@@ -165,6 +165,27 @@ __device__ __forceinline__ typename DT::V8 tr_pair_imm(uint32_t a_lo, uint32_t a
   const u32x2 hi = tr_read_imm<OFF>(a_hi);
   return as_v8<DT>(lo, hi);
 }
+// A 16-byte LDS read issued as inline assembly with a compile-time byte offset
+// (outside the compiler's view, like tr_read_imm); valid after lds_wait_n().
+template <int OFF>
+__device__ __forceinline__ u32x4 rd128_imm(uint32_t vaddr) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset field");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(vaddr), "n"(OFF));
+  return r;
+}
+// Wait until at most N LDS operations of this wave are outstanding. LDS
+// operations complete in issue order, so every read issued more than N LDS
+// operations ago has its result; the operands are tied through the wait so
+// that no use of them is scheduled before it.
+template <int N, class V>
+__device__ __forceinline__ void lds_wait_n(V& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N, class V>
+__device__ __forceinline__ void lds_wait_n4(V& a, V& b, V& c, V& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
 // Wait for every outstanding LDS read of this wave; the operands are tied
 // through the wait so that no use of them is scheduled before it.
 template <class V>
