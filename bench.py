@@ -452,6 +452,84 @@ def run_dense(w, dr, steps: int, warmup: int, pdrop: float = 0.0):
     return out
 
 
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
+
+
+def sweep(steps: int, warmup: int) -> dict:
+    """The metric's sweep: N = 1k..64k x d in {64, 128} x {non-causal, causal} x
+    bf16 (and fp16 at d = 64), H = 2048 / d heads, B = max(1, 16384 / N), so
+    every row holds 16384 tokens per head group. Inputs are N(0, 1) values drawn
+    on the device from a seeded generator (2000 + row index) and rounded to the
+    dtype; only timing is taken here (the parity tests cover the numbers).
+    TFLOP/s under the same convention as the headline (4d + 10d per kept pair)."""
+    import torch
+    from exact_io_aware_04_amd import fa, metrics
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    rows, idx = [], 0
+    for d in (64, 128):
+        for dname in (("bf16", "f16") if d == 64 else ("bf16",)):
+            tdt = torch.float16 if dname == "f16" else torch.bfloat16
+            dt = fa.FA_F16 if dname == "f16" else fa.FA_BF16
+            for causal in (False, True):
+                for N in SWEEP_N:
+                    H, B = 2048 // d, max(1, 16384 // N)
+                    g = torch.Generator(device=dev).manual_seed(2000 + idx)
+                    idx += 1
+                    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device=dev).to(tdt) for _ in range(4))
+                    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+                    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+                    Dv = torch.empty_like(lse)
+                    scale = 1.0 / math.sqrt(d)
+                    P = (q.data_ptr(), k.data_ptr(), v.data_ptr())
+
+                    def fwd():
+                        return fa.fa_fwd(*P, o.data_ptr(), lse.data_ptr(), B, H, N, d, dt, scale, int(causal), None, 128, st)
+
+                    def pre():
+                        return fa.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), Dv.data_ptr(), B, H, N, d, dt, st)
+
+                    def bwd():
+                        return fa.fa_bwd(*P, do.data_ptr(), lse.data_ptr(), Dv.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                         dv.data_ptr(), B, H, N, d, dt, scale, int(causal), None, 128, st)
+
+                    for _ in range(warmup):
+                        assert fwd() == 0 and pre() == 0 and bwd() == 0
+                    torch.cuda.synchronize()
+                    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+                    for e in ev:
+                        e[0].record(stream)
+                        fwd()
+                        e[1].record(stream)
+                        pre()
+                        e[2].record(stream)
+                        bwd()
+                        e[3].record(stream)
+                    torch.cuda.synchronize()
+                    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+                    b_ms = sum(e[1].elapsed_time(e[3]) for e in ev) / steps
+                    pairs = metrics.kept_pairs_per_head(N, causal, None) * B * H
+                    ff, fb = 4 * d * pairs, 10 * d * pairs
+                    tot = (ff + fb) / ((f_ms + b_ms) * 1e-3) / 1e12
+                    rows.append({"N": N, "d": d, "dtype": dname, "causal": causal, "B": B, "H": H,
+                                 "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                                 "fwd_tflops": round(ff / (f_ms * 1e-3) / 1e12, 1),
+                                 "bwd_tflops": round(fb / (b_ms * 1e-3) / 1e12, 1),
+                                 "tflops": round(tot, 1),
+                                 "pct_of_peak": round(100 * tot / metrics.MI355X_PEAK_DENSE_F16_TFLOPS, 2)})
+                    log(f"[sweep] N={N} d={d} {dname} causal={causal}: {tot:.1f} TFLOP/s "
+                        f"({rows[-1]['pct_of_peak']}%)")
+                    del q, k, v, do, o, dq, dk, dv, lse, Dv
+                    torch.cuda.empty_cache()
+    target = [r for r in rows if r["N"] >= 4096]
+    return {"metric": METRIC, "mode": "sweep", "data": "synthetic", "steps": steps, "warmup": warmup,
+            "rows": rows,
+            "n_ge_4096": {"rows": len(target),
+                          "min_pct_of_peak": min(r["pct_of_peak"] for r in target),
+                          "max_pct_of_peak": max(r["pct_of_peak"] for r in target)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,6 +542,9 @@ def main() -> int:
                     help="time budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other N >= 4096 workloads reported beside the default one")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the metric's sweep (N = 1k..64k, d = 64/128, causal and not) and print it "
+                         "as one JSON object instead of the headline line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -473,6 +554,9 @@ def main() -> int:
 
     import attn_inputs as ai
 
+    if args.sweep:
+        print(json.dumps(sweep(args.steps, args.warmup)), flush=True)
+        return 0
     if args.workload in ai.PACKED_WORKLOADS:
         return bench_packed(args, ai.PACKED_WORKLOADS[args.workload])
     if args.workload not in ai.WORKLOADS:
