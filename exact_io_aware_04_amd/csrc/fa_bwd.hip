@@ -81,8 +81,10 @@ __global__ __launch_bounds__(NW * 64, DkdvOccupancy<D>::value) void dkdv_kernel(
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.k_blocks);
-  const int bh = logical / p.k_blocks;        // (sequence, key/value head)
-  const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
+  int bh = logical / p.k_blocks;              // (sequence, key/value head)
+  int kb = logical - bh * p.k_blocks;         // causal: low key blocks carry the most rows, run first
+  if (p.causal && p.L.cu_q == nullptr && (long long)N * D <= kRankedMaxNd)
+    xcd_remap_ranked(blockIdx.x, p.total_blocks, p.k_blocks, bh, kb);
   const int k0 = kb * BK;
   const int kw0 = k0 + wave * 32;
   const int kw = kw0 + l32;                   // this lane's key (column of S and dP)
@@ -339,8 +341,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_split_kernel(BwdParams p) {
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.k_blocks);
-  const int bh = logical / p.k_blocks;        // (sequence, key/value head)
-  const int kb = logical - bh * p.k_blocks;   // causal: low key blocks carry the most rows, run first
+  int bh = logical / p.k_blocks;              // (sequence, key/value head)
+  int kb = logical - bh * p.k_blocks;         // causal: low key blocks carry the most rows, run first
+  if (p.causal && p.L.cu_q == nullptr && (long long)N * D <= kRankedMaxNd)
+    xcd_remap_ranked(blockIdx.x, p.total_blocks, p.k_blocks, bh, kb);
   const int k0 = kb * BK;
   const int kw0 = k0 + grp * 32;
   const int kw = kw0 + l32;                   // this lane's key
@@ -661,9 +665,15 @@ __global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_ker
   const int N = p.N;
 
   const int logical = xcd_remap(blockIdx.x, p.total_blocks, p.q_blocks);
-  const int bh = logical / p.q_blocks;
+  int bh = logical / p.q_blocks;
   int qb = logical - bh * p.q_blocks;
-  if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
+  if (p.causal) {                             // longest rows first
+    int rank;
+    if (p.L.cu_q == nullptr && (long long)N * D <= kRankedMaxNd &&
+        xcd_remap_ranked(blockIdx.x, p.total_blocks, p.q_blocks, bh, rank))
+      qb = rank;
+    qb = p.q_blocks - 1 - qb;
+  }
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 + l32;        // this lane's query
   const int b = bh / p.H, h = bh - b * p.H;

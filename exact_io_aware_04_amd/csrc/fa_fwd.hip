@@ -77,9 +77,15 @@ __global__ __launch_bounds__(NW * 64, (FwdOccupancy<D, DROP>::value)) void fwd_k
     split = logical % p.n_splits;
     logical /= p.n_splits;
   }
-  const int bh = logical / p.q_blocks;
+  int bh = logical / p.q_blocks;
   int qb = logical - bh * p.q_blocks;
-  if (p.causal) qb = p.q_blocks - 1 - qb;     // longest rows first
+  if (p.causal) {                             // longest rows first
+    int rank;
+    if (!SPLIT && p.L.cu_q == nullptr && (long long)N * D <= kRankedMaxNd &&
+        xcd_remap_ranked(blockIdx.x, p.total_blocks, p.q_blocks, bh, rank))
+      qb = rank;
+    qb = p.q_blocks - 1 - qb;
+  }
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 + l32;        // this lane's row (split-KV: group-packed row)
   const int HB = SPLIT ? p.L.Hk : p.H;        // heads the grid enumerates
