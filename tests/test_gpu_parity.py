@@ -216,6 +216,25 @@ def test_grid_with_partial_round_of_heads(causal):
         report(what, check_grads(_grads(res, 0, h), ref, what, ref["scales"], ai.F16))
 
 
+@pytest.mark.parametrize("B,H,n,d,dtype", [(2, 8, 1000, 128, ai.BF16), (3, 8, 300, 64, ai.F16)])
+def test_causal_ranked_block_order(B, H, n, d, dtype):
+    """Causal heads short enough for the ranked block order (N d <= 2^19, 16 and
+    24 heads: two and three heads per XCD, run rank by rank across them) in all
+    three kernels, every head compared whole against the oracle."""
+    say(f"[ranked order] B={B} H={H} N={n} d={d} {dtype}")
+    dr = ai.draw(B, H, n, d, dtype, 8_800 + n + d)
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, True, None)
+    for b in range(B):
+        for h in range(H):
+            ref = _oracle_head(dr, b, h, scale, True, None)
+            what = f"head ({b},{h})"
+            check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], dtype, what)
+            errs = check_grads(_grads(res, b, h), ref, what, ref["scales"], dtype)
+            if h == 0:
+                report(what, errs)
+
+
 def test_forward_is_bitwise_deterministic():
     import torch
     from exact_io_aware_04_amd import fa
