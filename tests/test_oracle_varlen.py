@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.dropout as od
 import oracle.varlen as ov
 
 
@@ -197,3 +198,68 @@ def test_merge_forms_agree():
                                      [a1[0] + np.log(a1[1]), a2[0] + np.log(a2[1])])
     np.testing.assert_allclose(o, acc / ell[:, None], rtol=1e-13)
     np.testing.assert_allclose(lse, m + np.log(ell), rtol=1e-13)
+
+
+# ---- dropout on packed batches (oracle.dropout per sequence and head)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_equal_lengths_match_dense_dropout(causal):
+    """Equal-length packed batch with dropout == the dense dropout oracle: the
+    mask of query head h of sequence b is that of dense head b H + h."""
+    B, H, N, d = 3, 2, 9, 8
+    rng = np.random.default_rng(6)
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    p, seed, off = 0.3, 0xABCDEF12345, 5
+    o, lse = od.forward(q, k, v, 0.5, causal, p, seed, off)
+    dq, dk, dv, dd = od.backward(q, k, v, do, 0.5, causal, p, seed, off)
+    pk = lambda x: x.transpose(0, 2, 1, 3).reshape(B * N, H, d)
+    cu = np.arange(B + 1) * N
+    o2, lse2 = ov.forward(pk(q), pk(k), pk(v), cu, cu, 0.5, causal, p, seed, off)
+    g2 = ov.backward(pk(q), pk(k), pk(v), pk(do), cu, cu, 0.5, causal, p, seed, off)
+    np.testing.assert_allclose(o2, pk(o), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse.transpose(0, 2, 1).reshape(B * N, H), rtol=1e-13)
+    for a, b_ in zip(g2[:3], (dq, dk, dv)):
+        np.testing.assert_allclose(a, pk(b_), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g2[3], dd.transpose(0, 2, 1).reshape(B * N, H), rtol=1e-12, atol=1e-12)
+    # and it differs from the run without dropout
+    o0, _ = ov.forward(pk(q), pk(k), pk(v), cu, cu, 0.5, causal)
+    assert np.abs(o0 - o2).max() > 1e-3
+
+
+def test_dropout_grouped_heads_equal_repeated_heads():
+    """With dropout, a shared key/value head still collects the gradients of
+    every query head that reads it, each query head with its own mask."""
+    q, k, v, do, cu_q, cu_k = _case(8, [5, 3, 0], [6, 8, 2], 6, 2)
+    grp = 3
+    kr, vr = np.repeat(k, grp, axis=1), np.repeat(v, grp, axis=1)
+    p, seed = 0.25, 99
+    for causal in (False, True):
+        o, lse = ov.forward(q, k, v, cu_q, cu_k, 0.4, causal, p, seed)
+        o_r, lse_r = ov.forward(q, kr, vr, cu_q, cu_k, 0.4, causal, p, seed)
+        np.testing.assert_allclose(o, o_r, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_r, rtol=1e-13)
+        dq, dk, dv, _ = ov.backward(q, k, v, do, cu_q, cu_k, 0.4, causal, p, seed)
+        dq_r, dk_r, dv_r, _ = ov.backward(q, kr, vr, do, cu_q, cu_k, 0.4, causal, p, seed)
+        np.testing.assert_allclose(dq, dq_r, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dk, dk_r.reshape(dk.shape[0], 2, grp, -1).sum(axis=2), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dv, dv_r.reshape(dv.shape[0], 2, grp, -1).sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+def test_dropout_packed_causal_alignment_uses_positions_in_the_sequence():
+    """Causal packed rows with fewer queries than keys: row i of sequence b
+    matches the dense dropout head of b Hq + h at query position i, keys
+    0..n_k-1, with the diagonal moved by n_k - n_q."""
+    q, k, v, do, cu_q, cu_k = _case(9, [3, 4], [7, 4], 2, 2)
+    p, seed, off = 0.4, 7, 3
+    o, lse = ov.forward(q, k, v, cu_q, cu_k, 0.6, True, p, seed, off)
+    sq, eq, sk, ek = int(cu_q[0]), int(cu_q[1]), int(cu_k[0]), int(cu_k[1])
+    o_h, lse_h = od.forward_head(q[sq:eq, 1], k[sk:ek, 1], v[sk:ek, 1], 0.6, True, p, seed, off, 0 * 2 + 1,
+                                 diag_offset=(ek - sk) - (eq - sq))
+    np.testing.assert_allclose(o[sq:eq, 1], o_h, rtol=1e-13, atol=1e-13)
+    sq, eq, sk, ek = int(cu_q[1]), int(cu_q[2]), int(cu_k[1]), int(cu_k[2])
+    keep = od.keep_mask(1 * 2 + 0, np.arange(eq - sq), np.arange(ek - sk), p, seed, off)
+    # the second sequence's head 0 uses the mask rows 0..3 of head 2, not the packed row numbers
+    o_h, _ = od.forward_head(q[sq:eq, 0], k[sk:ek, 0], v[sk:ek, 0], 0.6, True, p, seed, off, 2, diag_offset=0)
+    np.testing.assert_allclose(o[sq:eq, 0], o_h, rtol=1e-13, atol=1e-13)
+    assert keep.shape == (4, 4) and not keep.all()
