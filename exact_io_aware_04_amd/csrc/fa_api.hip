@@ -145,10 +145,10 @@ fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, f
                    "fa_fwd_dropout");
 }
 
-fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                        const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
-                        int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
-                        int causal, void* stream) {
+static fa_status fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                            int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                            int causal, const fa::Dropout& drop, void* stream, const char* where) {
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
   FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
   FA_TRY(check_dtype(dt));
@@ -168,7 +168,28 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   p.L.total_k = total_k;
   p.L.Hk = Hk;
   p.L.Nk = max_seqlen_k;
-  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_fwd_varlen");
+  p.drop = drop;
+  return hip_status(fa::launch_fwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), where);
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q, int total_k,
+                        int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale,
+                        int causal, void* stream) {
+  return fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                    max_seqlen_k, Hq, Hk, d, dt, scale, causal, fa::Dropout{}, stream, "fa_fwd_varlen");
+}
+
+fa_status fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                                int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d,
+                                fa_dtype dt, float scale, int causal, float p_drop, uint64_t seed, uint32_t offset,
+                                void* stream) {
+  fa::Dropout drop{};
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  FA_TRY(make_dropout(p_drop, seed, offset, &drop));
+  return fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q,
+                    max_seqlen_k, Hq, Hk, d, dt, scale, causal, drop, stream, "fa_fwd_varlen_dropout");
 }
 
 // Split-KV arguments other than the partial-result buffers.
@@ -337,11 +358,11 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const void
                    stream, "fa_bwd_dropout");
 }
 
-fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                        const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
-                        const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
-                        int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
-                        void* stream) {
+static fa_status bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                            const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                            const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                            int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                            const fa::Dropout& drop, void* stream, const char* where) {
   if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
     return FA_ERR_NULL;
   FA_TRY(check_varlen(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, Hq, Hk, d));
@@ -366,7 +387,32 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   p.L.total_k = total_k;
   p.L.Hk = Hk;
   p.L.Nk = max_seqlen_k;
-  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), "fa_bwd_varlen");
+  p.drop = drop;
+  return hip_status(fa::launch_bwd(p, dt == FA_BF16, reinterpret_cast<hipStream_t>(stream)), where);
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                        const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                        int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                        void* stream) {
+  return bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                    max_seqlen_q, max_seqlen_k, Hq, Hk, d, dt, scale, causal, fa::Dropout{}, stream,
+                    "fa_bwd_varlen");
+}
+
+fa_status fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                                const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                                const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                                float p_drop, uint64_t seed, uint32_t offset, void* stream) {
+  fa::Dropout drop{};
+  if (!q || !k || !v || !dO || !lse || !D || !dq || !dk || !dv || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_NULL;
+  FA_TRY(make_dropout(p_drop, seed, offset, &drop));
+  return bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                    max_seqlen_q, max_seqlen_k, Hq, Hk, d, dt, scale, causal, drop, stream,
+                    "fa_bwd_varlen_dropout");
 }
 
 const char* fa_status_string(fa_status s) {

@@ -6,7 +6,8 @@ stream. There is no fallback: if the shared library is missing or fails to
 load, importing this module raises.
 
 The low-level functions keep the C names (`fa_fwd`, `fa_bwd_preprocess`,
-`fa_bwd`, `fa_fwd_varlen`, `fa_bwd_varlen`, `fa_status_string`) and take
+`fa_bwd`, `fa_fwd_varlen`, `fa_bwd_varlen`, their `_dropout` forms,
+`fa_fwd_splitkv`, `fa_status_string`, ...) and take
 integer device addresses. `forward` / `backward` (dense [B, H, N, d]) and
 `forward_varlen` / `backward_varlen` (packed token-major, grouped heads) are
 thin conveniences over torch tensors that allocate the outputs and call the
@@ -31,7 +32,8 @@ STATUS = {
     -10: "FA_ERR_SCRATCH",
 }
 EXPORTED = ("fa_fwd", "fa_bwd_preprocess", "fa_bwd", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
-            "fa_bwd_varlen", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_status_string")
+            "fa_bwd_varlen", "fa_fwd_varlen_dropout", "fa_bwd_varlen_dropout", "fa_fwd_splitkv",
+            "fa_fwd_splitkv_noalloc", "fa_status_string")
 FA_MAX_SPLITS = 256
 FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -63,6 +65,11 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen_dropout.restype = i
+    lib.fa_fwd_varlen_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, f, u64, u32, vp]
+    lib.fa_bwd_varlen_dropout.restype = i
+    lib.fa_bwd_varlen_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
+                                          f, u64, u32, vp]
     lib.fa_fwd_splitkv.restype = i
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, i, vp, vp, vp]
     lib.fa_fwd_splitkv_noalloc.restype = i
@@ -120,6 +127,18 @@ def fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, t
                   d, dt, scale, causal, stream) -> int:
     return _lib.fa_bwd_varlen(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q,
                               max_k, Hq, Hk, d, dt, scale, causal, stream)
+
+
+def fa_fwd_varlen_dropout(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt,
+                          scale, causal, p_drop, seed, offset, stream) -> int:
+    return _lib.fa_fwd_varlen_dropout(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk,
+                                      d, dt, scale, causal, p_drop, seed, offset, stream)
+
+
+def fa_bwd_varlen_dropout(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq,
+                          Hk, d, dt, scale, causal, p_drop, seed, offset, stream) -> int:
+    return _lib.fa_bwd_varlen_dropout(q, k, v, dO, lse, D, dq, dk, dv, cu_q, cu_k, batch, total_q, total_k, max_q,
+                                      max_k, Hq, Hk, d, dt, scale, causal, p_drop, seed, offset, stream)
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, cu_q, cu_k, batch, total_q, total_k, max_q, max_k, Hq, Hk, d, dt, scale,
@@ -268,9 +287,11 @@ def _varlen_shapes(q, k, v, cu_q, cu_k):
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                   scale: Optional[float] = None, causal: bool = False, stream=None, out=None, lse=None):
+                   scale: Optional[float] = None, causal: bool = False, stream=None, out=None, lse=None,
+                   p_drop: float = 0.0, seed: int = 0, offset: int = 0):
     """fa_fwd_varlen on packed tensors q [total_q, Hq, d], k/v [total_k, Hk, d];
-    returns (o [total_q, Hq, d], lse [total_q, Hq]) (optionally into `out`, `lse`)."""
+    returns (o [total_q, Hq, d], lse [total_q, Hq]) (optionally into `out`, `lse`).
+    p_drop > 0 calls fa_fwd_varlen_dropout with (p_drop, seed, offset)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
     _expect(out, q.shape, q.dtype, q, "out")
@@ -280,16 +301,22 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     o = out if out is not None else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
-    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q),
-                       int(max_seqlen_k), hq, hk, d, _dt(q), float(scale), int(bool(causal)), _stream(stream))
-    _check(st, "fa_fwd_varlen")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+            cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hk, d, _dt(q),
+            float(scale), int(bool(causal)))
+    if p_drop > 0:
+        _check(fa_fwd_varlen_dropout(*args, float(p_drop), int(seed), int(offset), _stream(stream)),
+               "fa_fwd_varlen_dropout")
+    else:
+        _check(fa_fwd_varlen(*args, _stream(stream)), "fa_fwd_varlen")
     return o, lse
 
 
 def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                    scale: Optional[float] = None, causal: bool = False, stream=None, out=None):
-    """fa_bwd_preprocess over the packed rows, then fa_bwd_varlen; returns (dq, dk, dv, D).
+                    scale: Optional[float] = None, causal: bool = False, stream=None, out=None,
+                    p_drop: float = 0.0, seed: int = 0, offset: int = 0):
+    """fa_bwd_preprocess over the packed rows, then fa_bwd_varlen (fa_bwd_varlen_dropout
+    when p_drop > 0: the forward's p_drop, seed, offset); returns (dq, dk, dv, D).
     `out` = optional (dq, dk, dv)."""
     torch = _torch()
     batch, tq, tk, hq, hk, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
@@ -305,11 +332,13 @@ def backward_varlen(q, k, v, o, lse, dO, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if tq > 0:
         _check(fa_bwd_preprocess(o.data_ptr(), dO.data_ptr(), D.data_ptr(), 1, hq, tq, d, dt, s), "fa_bwd_preprocess")
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
-                       cu_seqlens_k.data_ptr(), batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hk, d,
-                       dt, float(scale), int(bool(causal)), s)
-    _check(st, "fa_bwd_varlen")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dO.data_ptr(), lse.data_ptr(), D.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), batch, tq, tk,
+            int(max_seqlen_q), int(max_seqlen_k), hq, hk, d, dt, float(scale), int(bool(causal)))
+    if p_drop > 0:
+        _check(fa_bwd_varlen_dropout(*args, float(p_drop), int(seed), int(offset), s), "fa_bwd_varlen_dropout")
+    else:
+        _check(fa_bwd_varlen(*args, s), "fa_bwd_varlen")
     return dq, dk, dv, D
 
 

@@ -210,6 +210,27 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
                         void* stream);
 
+/* Dropout on packed batches [P1, key design 2 table and key design 3, as for
+ * fa_fwd_dropout; P2 usage section for the packed layout]: fa_fwd_varlen /
+ * fa_bwd_varlen with the mask of fa_fwd_dropout, where query head h of
+ * sequence b is mask head bh = b * Hq + h and i, j are the query and key
+ * positions inside the sequence (0 = its first row). dk, dv of a shared
+ * key/value head sum the contributions of the query heads that read it, each
+ * with its own mask. The same (p_drop, seed, offset) must be passed to the
+ * forward and the backward. FA_ERR_DROPOUT unless 0 <= p_drop < 1; p_drop = 0
+ * reproduces fa_fwd_varlen / fa_bwd_varlen bit for bit. */
+fa_status fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int total_q,
+                                int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hk, int d,
+                                fa_dtype dt, float scale, int causal, float p_drop, uint64_t seed, uint32_t offset,
+                                void* stream);
+
+fa_status fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                                const float* D, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                                const int* cu_seqlens_k, int batch, int total_q, int total_k, int max_seqlen_q,
+                                int max_seqlen_k, int Hq, int Hk, int d, fa_dtype dt, float scale, int causal,
+                                float p_drop, uint64_t seed, uint32_t offset, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -150,6 +150,35 @@ def test_bwd_varlen_validation(kw, code):
     assert bwd_varlen(**kw) == code
 
 
+def fwd_varlen_dropout(p_drop=0.1, seed=7, offset=0, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, cu_q=A, cu_k=A, batch=2, total_q=40, total_k=50, max_q=30, max_k=30,
+                Hq=4, Hk=2, d=64, dt=fa.FA_BF16, scale=0.125, causal=1)
+    args.update(kw)
+    return fa.fa_fwd_varlen_dropout(*args.values(), p_drop, seed, offset, None)
+
+
+def bwd_varlen_dropout(p_drop=0.1, seed=7, offset=0, **kw):
+    args = dict(q=A, k=A, v=A, dO=A, lse=A, D=A, dq=A, dk=A, dv=A, cu_q=A, cu_k=A, batch=2, total_q=40,
+                total_k=50, max_q=30, max_k=30, Hq=4, Hk=2, d=128, dt=fa.FA_F16, scale=0.125, causal=0)
+    args.update(kw)
+    return fa.fa_bwd_varlen_dropout(*args.values(), p_drop, seed, offset, None)
+
+
+VARLEN_DROPOUT_CASES = [(dict(p_drop=-0.1), -9), (dict(p_drop=1.0), -9), (dict(p_drop=float("nan")), -9),
+                        (dict(q=None, p_drop=float("nan")), -1)]
+
+
+@pytest.mark.parametrize("kw,code", VARLEN_CASES + VARLEN_DROPOUT_CASES)
+def test_fwd_varlen_dropout_validation(kw, code):
+    assert fwd_varlen_dropout(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [c for c in VARLEN_CASES if "o" not in c[0]] + VARLEN_DROPOUT_CASES + [
+    (dict(dk=None), -1), (dict(D=None), -1), (dict(dv=MIS), -6)])
+def test_bwd_varlen_dropout_validation(kw, code):
+    assert bwd_varlen_dropout(**kw) == code
+
+
 def fwd_splitkv(**kw):
     args = dict(q=A, k=A, v=A, o=A, lse=A, cu_q=A, cu_k=A, batch=2, total_q=2, total_k=5000, max_q=1, max_k=4096,
                 Hq=8, Hk=2, d=128, dt=fa.FA_BF16, scale=0.125, causal=0, n_splits=8, o_part=A, lse_part=A,

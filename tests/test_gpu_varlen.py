@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import attn_inputs as ai
+import oracle.dropout as od
 import oracle.varlen as ov
 from error_model import Scales, gradient_scales_head
 from harness import GRAD_REL_TOL, O_TOL, LSE_TOL, check_grads, from_dev, rel_fro, report, say, to_dev
@@ -32,7 +33,7 @@ def _dev_i32(a):
     return torch.from_numpy(np.asarray(a, dtype=np.int32)).cuda()
 
 
-def run_varlen(pk: ai.PackedDrawn, hq, hk, scale, causal):
+def run_varlen(pk: ai.PackedDrawn, hq, hk, scale, causal, p_drop=0.0, seed=0, offset=0):
     import torch
     from exact_io_aware_04_amd import fa
     q, k, v, do = (to_dev(getattr(pk, n), pk.dtype) for n in ("q", "k", "v", "do"))
@@ -42,25 +43,29 @@ def run_varlen(pk: ai.PackedDrawn, hq, hk, scale, causal):
     # outputs start as NaN: an element a kernel fails to write fails the comparison
     nan = lambda t: torch.full_like(t, float("nan"))
     lse0 = torch.full((q.shape[0], q.shape[1]), float("nan"), dtype=torch.float32, device=q.device)
-    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal, out=nan(q), lse=lse0)
+    drop = dict(p_drop=p_drop, seed=seed, offset=offset)
+    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale, causal, out=nan(q), lse=lse0, **drop)
     dq, dk, dv, D = fa.backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, scale, causal,
-                                       out=(nan(q), nan(k), nan(v)))
+                                       out=(nan(q), nan(k), nan(v)), **drop)
     torch.cuda.synchronize()
     return {"o": from_dev(o, pk.dtype), "lse": lse.double().cpu().numpy(), "dq": from_dev(dq, pk.dtype),
             "dk": from_dev(dk, pk.dtype), "dv": from_dev(dv, pk.dtype), "D": D.double().cpu().numpy(),
             "dev": (o, lse, dq, dk, dv)}
 
 
-def check_sequence_group(res, grads, q, k, v, do, cu_q, cu_k, b, g, grp, scale, causal, dtype, what):
+def check_sequence_group(res, grads, q, k, v, do, cu_q, cu_k, b, g, grp, scale, causal, dtype, what, zf=None):
     """Gradients of sequence b, key/value head g and its query heads against the
-    oracle's, element by element (grads = oracle dQ, dK, dV of the packed batch)."""
+    oracle's, element by element (grads = oracle dQ, dK, dV of the packed batch).
+    zf(h, rows, cols), under dropout, gives query head h's multiplier M / (1 - p)
+    at positions inside the sequence."""
     sq, eq, sk, ek = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
     heads = list(range(g * grp, (g + 1) * grp))
     parts = []
     for h in heads:
         if eq > sq and ek > sk:
+            z = None if zf is None else (lambda rows, cols, h=h: zf(h, rows, cols))
             parts.append(gradient_scales_head(q[sq:eq, h], k[sk:ek, g], v[sk:ek, g], do[sq:eq, h], scale, causal,
-                                              diag_offset=(ek - sk) - (eq - sq)))
+                                              diag_offset=(ek - sk) - (eq - sq), z=z))
     zq, zk = np.zeros((eq - sq, len(heads), q.shape[2])), np.zeros((ek - sk, q.shape[2]))
     sc = {
         "dq": Scales(*(np.stack([getattr(pp["dq"], f) for pp in parts], axis=1) if parts else zq
@@ -289,3 +294,88 @@ def test_packed_outputs_stay_inside_their_buffers(d, dtype, causal):
         assert (buf[:PAD] == 7.0).all() and (buf[-PAD:] == 7.0).all()
     for t in (o, dq, dk, dv):
         assert torch.isfinite(t).all()
+
+
+# ---- dropout on packed batches (fa_fwd_varlen_dropout / fa_bwd_varlen_dropout)
+
+DROP_SEED = 0x0DDB_A11_5EED
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,dtype", [(64, ai.F16), (128, ai.BF16)])
+@pytest.mark.parametrize("case", ["mixed_gqa", "more_q_than_k", "empty_seqs"])
+def test_varlen_dropout_parity(case, d, dtype, causal):
+    """Packed dropout against oracle/varlen.py with dropout: O and LSE per
+    element, gradients per (sequence, key/value head) under the rounding bound
+    with the keep mask of query head b Hq + h folded into the terms."""
+    lq, lk, hq, hk = CASES[case]
+    p, offset = 0.2, 5
+    seed = 40_000 + 13 * list(CASES).index(case) + d + (2 if causal else 0)
+    say(f"[varlen dropout] {case} d={d} {dtype} causal={causal} p={p} seed={seed}")
+    pk = ai.draw_packed(lq, lk, hq, hk, d, dtype, seed)
+    scale = 1.0 / np.sqrt(d)
+    res = run_varlen(pk, hq, hk, scale, causal, p, DROP_SEED + seed, offset)
+    q, k, v, do = (pk.f64(n) for n in ("q", "k", "v", "do"))
+    o_ref, lse_ref = ov.forward(q, k, v, pk.cu_q, pk.cu_k, scale, causal, p, DROP_SEED + seed, offset)
+    grads = ov.backward(q, k, v, do, pk.cu_q, pk.cu_k, scale, causal, p, DROP_SEED + seed, offset)
+    what = f"{case} d={d} {dtype} causal={causal} p={p}"
+    assert np.isfinite(res["o"]).all(), what
+    err = float(np.abs(res["o"] - o_ref).max())
+    assert err <= O_TOL[dtype] / (1 - p), f"{what}: O error {err:.3e}"
+    live = np.isfinite(lse_ref)
+    assert (np.isneginf(res["lse"]) == ~live).all(), f"{what}: LSE -inf pattern"
+    if live.any():
+        assert float(np.abs(res["lse"][live] - lse_ref[live]).max()) <= LSE_TOL[dtype], what
+    for b in range(len(lq)):
+        zf = lambda h, rows, cols, b=b: od.keep_mask(b * hq + h, rows, cols, p, DROP_SEED + seed, offset) / (1 - p)
+        for g in range(hk):
+            errs = check_sequence_group(res, grads, q, k, v, do, pk.cu_q, pk.cu_k, b, g, hq // hk, scale, causal,
+                                        dtype, what, zf)
+            if b == 0 and g == 0:
+                report(what, errs)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_dropout_matches_dense_dropout_bitwise(d, causal):
+    """Equal lengths and Hk == Hq: the packed dropout path gives the dense dropout
+    path's bits (mask head b H + h, positions inside the sequence), and p = 0
+    gives the packed path without dropout bit for bit."""
+    import torch
+    from exact_io_aware_04_amd import fa
+    B, H, N = 3, 2, 200
+    p, seed, off = 0.3, 4242 + d, 9
+    say(f"[varlen dropout vs dense] d={d} causal={causal}")
+    dr = ai.draw(B, H, N, d, ai.BF16, 919 + d + causal)
+    q, k, v, do = (to_dev(getattr(dr, n), dr.dtype) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward_dropout(q, k, v, p, seed, off, None, causal)
+    dq, dk, dv, D = fa.backward_dropout(q, k, v, o, lse, do, p, seed, off, None, causal)
+    pk = lambda x: x.transpose(1, 2).contiguous().view(B * N, H, d)
+    cu = _dev_i32(np.arange(B + 1) * N)
+    o2, lse2 = fa.forward_varlen(pk(q), pk(k), pk(v), cu, cu, N, N, None, causal, p_drop=p, seed=seed, offset=off)
+    dq2, dk2, dv2, _ = fa.backward_varlen(pk(q), pk(k), pk(v), o2, lse2, pk(do), cu, cu, N, N, None, causal,
+                                          p_drop=p, seed=seed, offset=off)
+    o0, lse0 = fa.forward_varlen(pk(q), pk(k), pk(v), cu, cu, N, N, None, causal)
+    g0 = fa.backward_varlen(pk(q), pk(k), pk(v), o0, lse0, pk(do), cu, cu, N, N, None, causal)
+    dev_pk = (pk(q), pk(k), pk(v))
+    from exact_io_aware_04_amd.fa import FA_BF16, fa_bwd_preprocess, fa_bwd_varlen_dropout, fa_fwd_varlen_dropout
+    o3, lse3 = torch.empty_like(o0), torch.empty_like(lse0)
+    st = fa_fwd_varlen_dropout(*(t.data_ptr() for t in dev_pk), o3.data_ptr(), lse3.data_ptr(), cu.data_ptr(),
+                               cu.data_ptr(), B, B * N, B * N, N, N, H, H, d, FA_BF16, 1.0 / np.sqrt(d), int(causal),
+                               0.0, seed, off, None)
+    assert st == 0
+    D3 = torch.empty_like(lse0)
+    assert fa_bwd_preprocess(o3.data_ptr(), pk(do).data_ptr(), D3.data_ptr(), 1, H, B * N, d, FA_BF16, None) == 0
+    g3 = tuple(torch.empty_like(t) for t in dev_pk)
+    st = fa_bwd_varlen_dropout(*(t.data_ptr() for t in dev_pk), pk(do).data_ptr(), lse3.data_ptr(), D3.data_ptr(),
+                               *(t.data_ptr() for t in g3), cu.data_ptr(), cu.data_ptr(), B, B * N, B * N, N, N, H,
+                               H, d, FA_BF16, 1.0 / np.sqrt(d), int(causal), 0.0, seed, off, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o2, pk(o))
+    assert torch.equal(lse2, lse.transpose(1, 2).contiguous().view(B * N, H))
+    for a, b_ in ((dq2, dq), (dk2, dk), (dv2, dv)):
+        assert torch.equal(a, pk(b_))
+    assert torch.equal(o3, o0) and torch.equal(lse3, lse0)
+    for a, b_ in zip(g3, g0[:3]):
+        assert torch.equal(a, b_)
