@@ -676,6 +676,7 @@ __global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_ker
   }
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32 + l32;        // this lane's query
+  const int w0 = q0 + __builtin_amdgcn_readfirstlane(wave) * 32;   // this wave's first query
   const int b = bh / p.H, h = bh - b * p.H;
   const HeadView hv = head_view(p.L, b, h, p.H, N, D);
   const int lq = hv.lq, lk = hv.lk;
@@ -753,45 +754,48 @@ __global__ __launch_bounds__(NW * 64, (DqOccupancy<D, DROP>::value)) void dq_ker
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
     const int k0 = j * BN;
-    const bool edge = (k0 + BN > lk) || (p.causal && k0 + BN - 1 > q0 + off);
+    // a wave none of whose rows sees the tile only takes its part in the copies and barriers
+    if (w0 < lq && (!p.causal || k0 <= w0 + 31 + off)) {
+      const bool edge = (k0 + BN > lk) || (p.causal && k0 + BN - 1 > q0 + off);
 
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      // S^T and dP^T: rows = keys k0 + 32 t + mrow, column = this lane's query
-      f32x16 s = f32x16{}, dp = f32x16{};
+      for (int t = 0; t < NS; ++t) {
+        // S^T and dP^T: rows = keys k0 + 32 t + mrow, column = this lane's query
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        s = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s);
-        dp = DT::mma(as_v8<DT>(lds_read16(vt, koff[c] + 32 * t * ROWB)), of[c], dp);
-      }
-      float de[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) de[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
-      if (edge) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * t + mrow(g, r);
-          if (key >= lk || (p.causal && key > qw + off)) de[r] = 0.f;
+        for (int c = 0; c < KC; ++c) {
+          s = DT::mma(as_v8<DT>(lds_read16(kt, koff[c] + 32 * t * ROWB)), qf[c], s);
+          dp = DT::mma(as_v8<DT>(lds_read16(vt, koff[c] + 32 * t * ROWB)), of[c], dp);
         }
-      }
-      if constexpr (DROP) {                   // dP = Z o (dO V^T), Z = M / (1 - p)
-        // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u (as in the forward)
-        const uint32_t kb16 = keep16_pair(p.drop, (uint32_t)((k0 + 32 * t) >> 2), (uint32_t)qw, (uint32_t)bh, lane);
+        float de[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = ((kb16 >> r) & 1) ? dp[r] * p.drop.rescale : 0.f;
-      }
+        for (int r = 0; r < 16; ++r) de[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -lse2));
+        if (edge) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) de[r] *= dp[r] - dq_d;
-      V8 sb[2];
-      sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
-      sb[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
-      // dQ^T += K^T dS^T over these 32 keys
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * t + mrow(g, r);
+            if (key >= lk || (p.causal && key > qw + off)) de[r] = 0.f;
+          }
+        }
+        if constexpr (DROP) {                 // dP = Z o (dO V^T), Z = M / (1 - p)
+          // keys k0 + 32 t + 8 jj + 4 g + u sit in register 4 jj + u (as in the forward)
+          const uint32_t kb16 = keep16_pair(p.drop, (uint32_t)((k0 + 32 * t) >> 2), (uint32_t)qw, (uint32_t)bh, lane);
 #pragma unroll
-      for (int dt = 0; dt < DT32; ++dt) {
+          for (int r = 0; r < 16; ++r) dp[r] = ((kb16 >> r) & 1) ? dp[r] * p.drop.rescale : 0.f;
+        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          acc[dt] = DT::mma(tr_pair<DT>(kt, ktoff[dt][0] + (32 * t + 16 * h) * ROWB,
-                                        ktoff[dt][1] + (32 * t + 16 * h) * ROWB), sb[h], acc[dt]);
+        for (int r = 0; r < 16; ++r) de[r] *= dp[r] - dq_d;
+        V8 sb[2];
+        sb[0] = pack8<DT>(de[0], de[1], de[2], de[3], de[4], de[5], de[6], de[7]);
+        sb[1] = pack8<DT>(de[8], de[9], de[10], de[11], de[12], de[13], de[14], de[15]);
+        // dQ^T += K^T dS^T over these 32 keys
+#pragma unroll
+        for (int dt = 0; dt < DT32; ++dt) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[dt] = DT::mma(tr_pair<DT>(kt, ktoff[dt][0] + (32 * t + 16 * h) * ROWB,
+                                          ktoff[dt][1] + (32 * t + 16 * h) * ROWB), sb[h], acc[dt]);
+        }
       }
     }
 
