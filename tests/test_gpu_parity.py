@@ -83,6 +83,32 @@ def _rescales_per_row(s_scaled, causal, tile=64, threshold=8.0):
     return counts
 
 
+def check_forward_rounding(o, dr, b, h, scale, causal, ref, dtype, what):
+    """O against the oracle under its rounding bound, and under the stated max-abs
+    tolerance (2e-3 fp16, 1e-2 bf16) wherever that bound is within it. The PV
+    product consumes the probabilities rounded to the operand type (RNE, unit
+    roundoff u), which moves O_ic by at most u sum_j P_ij |V_jc - O_ic| <=
+    u ((P |V|)_ic + |O_ic|) (the weights stay normalised), and O itself is
+    rounded (u |O_ic|); a wrong rescale factor or a wrong tile errs by O(1). A
+    bf16 output with |O| >= 2.56 can round by more than 1e-2 on its own."""
+    u = UNIT_ROUNDOFF[dtype]
+    q, k, v = (dr.f64(x, b, h) for x in "qkv")
+    n = q.shape[0]
+    sc = scale * (q @ k.T)
+    if causal:
+        sc = np.where(np.tril(np.ones((n, n), dtype=bool)), sc, -np.inf)
+    p = np.exp(sc - ref["lse"][:, None])
+    bound = u * (p @ np.abs(v) + 2.0 * np.abs(ref["o"])) + 1e-4
+    assert np.isfinite(o).all(), what
+    err = np.abs(o - ref["o"])
+    inside = bound <= O_TOL[dtype]
+    say(f"    {what}: O max-abs error {err.max():.3e} (rounding bound up to {bound.max():.3e}); "
+        f"{inside.mean() * 100:.1f}% of elements have a bound within {O_TOL[dtype]:g}, "
+        f"max error there {err[inside].max() if inside.any() else 0.0:.3e}")
+    assert (err <= bound).all(), f"{what}: O error {err.max():.3e} beyond the rounding bound"
+    assert (err[inside] <= O_TOL[dtype]).all(), f"{what}: O error beyond the stated tolerance"
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [ai.F16, ai.BF16])
 @pytest.mark.parametrize("d", [64, 128])
@@ -99,31 +125,10 @@ def test_running_max_keeps_rising(d, dtype, causal):
     fired = _rescales_per_row(scale * (q0 @ k0.T), causal)
     assert fired[n // 2:].mean() >= 2.0, f"inputs exercise too few rescales ({fired.mean():.2f} per row)"
     res = run_gpu(dr, scale, causal, None, backward=True)
-    # O bound for a softmax this peaked: the PV product consumes the probabilities
-    # rounded to the operand type (RNE, unit roundoff u), which moves O_ic by at most
-    # u sum_j P_ij |V_jc - O_ic| <= u ((P |V|)_ic + |O_ic|) (the weights stay
-    # normalised), and O itself is rounded (u |O_ic|). A wrong rescale factor errs by
-    # O(1). Where that rounding bound is within the stated O tolerance (2e-3 fp16,
-    # 1e-2 bf16), the stated tolerance itself is asserted.
-    u = UNIT_ROUNDOFF[dtype]
     for h in range(2):
         ref = _oracle_head(dr, 0, h, scale, causal, None)
         what = f"rescale N={n} d={d} {dtype} causal={causal} h={h}"
-        q, k, v = (dr.f64(x, 0, h) for x in "qkv")
-        sc = scale * (q @ k.T)
-        if causal:
-            sc = np.where(np.tril(np.ones((n, n), dtype=bool)), sc, -np.inf)
-        p = np.exp(sc - ref["lse"][:, None])
-        bound = u * (p @ np.abs(v) + 2.0 * np.abs(ref["o"])) + 1e-4
-        o = res["o"][0, h]
-        assert np.isfinite(o).all(), what
-        err = np.abs(o - ref["o"])
-        inside = bound <= O_TOL[dtype]
-        say(f"    {what}: O max-abs error {err.max():.3e} (rounding bound up to {bound.max():.3e}); "
-            f"{inside.mean() * 100:.1f}% of elements have a bound within {O_TOL[dtype]:g}, "
-            f"max error there {err[inside].max() if inside.any() else 0.0:.3e}")
-        assert (err <= bound).all(), f"{what}: O error {err.max():.3e} beyond the rounding bound"
-        assert (err[inside] <= O_TOL[dtype]).all(), f"{what}: O error beyond the stated tolerance"
+        check_forward_rounding(res["o"][0, h], dr, 0, h, scale, causal, ref, dtype, what)
         assert np.abs(res["lse"][0, h] - ref["lse"]).max() <= LSE_TOL[dtype], f"{what}: LSE"
         report(what, check_grads(_grads(res, 0, h), ref, what, ref["scales"], dtype))
 
@@ -232,6 +237,29 @@ def test_causal_ranked_block_order(B, H, n, d, dtype):
             check_forward(res["o"][b, h], res["lse"][b, h], ref["o"], ref["lse"], dtype, what)
             errs = check_grads(_grads(res, b, h), ref, what, ref["scales"], dtype)
             if h == 0:
+                report(what, errs)
+
+
+@pytest.mark.parametrize("dtype,causal", [(ai.BF16, True), (ai.F16, False)])
+def test_wide_blocks_short_heads(dtype, causal):
+    """64 heads of N = 1024 at d = 128: 256 blocks of 256 query rows, the
+    smallest grid that runs the 8-wave forward and dQ workgroups (with the
+    ranked block order when causal); every head compared whole against the
+    oracle."""
+    B, H, n, d = 4, 16, 1024, 128
+    say(f"[8-wave blocks] B={B} H={H} N={n} d={d} {dtype} causal={causal}")
+    dr = ai.draw(B, H, n, d, dtype, 9_100 + int(causal))
+    scale = 1.0 / np.sqrt(d)
+    res = run_gpu(dr, scale, causal, None)
+    for b in range(B):
+        for h in range(H):
+            ref = _oracle_head(dr, b, h, scale, causal, None)
+            what = f"head ({b},{h})"
+            check_forward_rounding(res["o"][b, h], dr, b, h, scale, causal, ref, dtype, what)
+            lerr = np.abs(res["lse"][b, h] - ref["lse"]).max()
+            assert lerr <= LSE_TOL[dtype], f"{what}: LSE max-abs error {lerr:.3e}"
+            errs = check_grads(_grads(res, b, h), ref, what, ref["scales"], dtype)
+            if b == 0 and h == 0:
                 report(what, errs)
 
 
