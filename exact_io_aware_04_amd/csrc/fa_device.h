@@ -33,6 +33,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Largest N d of a dense head whose causal grid runs ranked (xcd_remap_ranked).
 constexpr long long kRankedMaxNd = 1ll << 19;
+// The 8-wave (256-row) forward and dQ workgroups are used when there are at least
+// this many of them, one per compute unit; smaller grids run twice as many 4-wave
+// workgroups instead.
+constexpr long long kWideMinBlocks = 256;
 
 struct F16 {
   using T = _Float16;

@@ -458,16 +458,21 @@ hipError_t launch_fwd(const FwdParams& p, int is_bf16, hipStream_t st) {
   if (p.D == 64) {
     // d = 64, dense layout, without causal masking, block mask or dropout: 8-wave workgroups (256 query
     // rows) share each K/V tile, halving the tile copies per product (with causal masking
-    // the coarser diagonal costs more than that saves)
-    if (!p.causal && p.mask == nullptr && !p.drop.on && p.L.cu_q == nullptr)
+    // the coarser diagonal costs more than that saves); grids of fewer than kWideMinBlocks
+    // such workgroups run twice as many 4-wave ones
+    if (!p.causal && p.mask == nullptr && !p.drop.on && p.L.cu_q == nullptr &&
+        (long long)p.B * p.H * ((p.N + 255) / 256) >= kWideMinBlocks)
       return is_bf16 ? launch_fwd_t<BF16, 64, 64, 8>(p, st) : launch_fwd_t<F16, 64, 64, 8>(p, st);
     return is_bf16 ? launch_fwd_t<BF16, 64, 64, 4>(p, st) : launch_fwd_t<F16, 64, 64, 4>(p, st);
   }
   // d = 128, dense layout, without block mask or dropout: 8-wave workgroups (256 query
   // rows) share each K/V tile (causal N=65536: 7.75 -> 7.50 ms, N=8192: 1.10 -> 1.08 ms;
   // a packed batch of sequences up to 4096 long loses more in ragged ends:
-  // 0.96 -> 1.16 ms)
-  if (p.mask == nullptr && !p.drop.on && p.L.cu_q == nullptr)
+  // 0.96 -> 1.16 ms). Grids of fewer than kWideMinBlocks such workgroups leave compute
+  // units idle and run twice as many 4-wave ones instead (causal B1 H8 N4096:
+  // 0.100 -> 0.075 ms; B3 H5 N1000: 0.032 -> 0.024 ms).
+  if (p.mask == nullptr && !p.drop.on && p.L.cu_q == nullptr &&
+      (long long)p.B * p.H * ((p.N + 255) / 256) >= kWideMinBlocks)
     return is_bf16 ? launch_fwd_t<BF16, 128, 64, 8>(p, st) : launch_fwd_t<F16, 128, 64, 8>(p, st);
   return is_bf16 ? launch_fwd_t<BF16, 128, 64, 4>(p, st) : launch_fwd_t<F16, 128, 64, 4>(p, st);
 }
