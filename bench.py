@@ -392,6 +392,10 @@ def run_dense(w, dr, steps: int, warmup: int, pdrop: float = 0.0):
         bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
     else:
         pre_ms = bwd_ms = 0.0
+    # per-step GPU time on the launch stream (first to last event of each step)
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in ev)
+    step_ms = {"median": round(float(np.median(per_step)), 4), "min": round(per_step[0], 4),
+               "max": round(per_step[-1], 4)}
 
     pairs = metrics.kept_pairs_per_head(N, w.causal, mask)
     f_fwd, f_bwd = metrics.flops(B, H, pairs, d)
@@ -434,6 +438,7 @@ def run_dense(w, dr, steps: int, warmup: int, pdrop: float = 0.0):
     out = {
         "value": round(value, 2),
         "ms_per_step": round(ms_step, 4),
+        "step_ms": step_ms,
         "pct_of_peak": round(100 * value / peak, 2),
         "phases_ms": {"fwd": round(fwd_ms, 4), "bwd_preprocess": round(pre_ms, 4), "bwd": round(bwd_ms, 4)},
         "phase_tflops": {"fwd": round(fwd_tf, 2), "bwd": round(bwd_tf, 2) if bwd_tf else None},
@@ -589,8 +594,8 @@ def main() -> int:
         "data": "synthetic",
         "config": head["config"],
     }
-    result.update({k: head[k] for k in ("pct_of_peak", "phases_ms", "phase_tflops", "bytes_model", "memory",
-                                        "roofline")})
+    result.update({k: head[k] for k in ("step_ms", "pct_of_peak", "phases_ms", "phase_tflops", "bytes_model",
+                                        "memory", "roofline")})
     result["cpu_baseline"] = cpu
     if args.workload == DEFAULT_WORKLOAD and pdrop == 0 and not args.no_extra:
         others = {}
